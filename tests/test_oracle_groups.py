@@ -1,0 +1,225 @@
+"""Pins for the oracle's per-group paths (group map, amax, scale, cast).
+
+* Hand-worked tensors (tests/golden/hand_worked.json): boundaries with an
+  empty group, all-zero slices, signs, the pow2 rounding direction, scale
+  layouts (G, K) for dim0 and (M, G) for dim1.
+* Scale: each stored scale is checked with exact rational arithmetic to be
+  the binary32 value nearest to 448 / max(amax, 1e-12), and in pow2 mode
+  the largest power of two not above it.
+* Invariants on seeded tensors: the slice maximum lands on +-448 (0x7E /
+  0xFE), every code is within half an E4M3 step of fl32(x * s), sign kept.
+* Locality: changing one group's rows leaves every other group untouched.
+* The transpose identity of the rowwise page's Summary:
+  dim1(T transposed) == dim0(T) transposed, bit for bit.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import golden_io
+from group_scaling_fp8_amd import workloads as wl
+
+EPS32 = float(np.float32(1e-12))
+
+
+def decode_table():
+    t = np.zeros(256)
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            t[c] = np.nan
+            continue
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        t[c] = -v if s else v
+    return t
+
+
+DEC = decode_table()
+
+
+def half_step(v):
+    """Half the E4M3 grid spacing around |v| (|v| <= 448)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 0.5 * 2.0 ** (e - 3)
+
+
+def f32(bits):
+    return np.asarray(bits, dtype=np.uint32).view(np.float32)
+
+
+# ---------------------------------------------------------------- goldens
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("case", ["dim0_single_column", "dim0_groups"])
+def test_dim0_golden(oracle_mod, case, pow2):
+    g = golden_io.load()[case]
+    x = golden_io.dense_bits(g["x"])
+    q, s = oracle_mod.quant_groups_dim0(x, np.array(g["offsets"], np.int32), pow2)
+    want = g["pow2"]["true" if pow2 else "false"]
+    assert np.array_equal(s.view(np.uint32), golden_io.hex_matrix_u32(want["scales"]))
+    assert np.array_equal(q, golden_io.hex_matrix_u8(want["q"]))
+
+
+def test_dim1_golden(oracle_mod):
+    g = golden_io.load()["dim1_groups"]
+    x = golden_io.sparse_bits(g["x_sparse"])
+    q, s = oracle_mod.quant_groups_dim1(x, np.array(g["offsets"], np.int32))
+    assert np.array_equal(s.view(np.uint32), golden_io.hex_matrix_u32(g["scales"]))
+    assert np.array_equal(q, golden_io.sparse_q(x.shape, g["q_sparse"], g["q_default"]))
+
+
+# ---------------------------------------------------------- scale (exact)
+
+
+def nearest_f32(fr):
+    """binary32 value nearest to the positive rational fr (ties to even),
+    found by comparing against the two neighbouring binary32 values."""
+    c = np.float32(float(fr))           # float() rounds correctly to binary64
+    best = None
+    for cand in (np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - fr)
+        key = (d, int(np.array(cand, np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return np.float32(best[1])
+
+
+def test_scale_is_correctly_rounded_quotient(oracle_mod):
+    rng = np.random.default_rng(7)
+    bits = np.concatenate([rng.integers(1, 0x7F80, 3000), [0, 1, 0x3F80, 0x4040, 0x2B8C, 0x2B8D]])
+    for b in bits:
+        a = float(f32(np.uint32(b) << np.uint32(16)))
+        den = max(Fraction(a), Fraction(EPS32))
+        s = oracle_mod.group_scale(a, False)
+        assert np.float32(s) == nearest_f32(Fraction(448) / den), hex(b)
+        p = Fraction(oracle_mod.group_scale(a, True))
+        assert p.numerator == 1 or p.denominator == 1            # power of two
+        assert p <= Fraction(s) < 2 * p
+
+
+def test_zero_and_empty_scale_constants(oracle_mod):
+    assert np.float32(oracle_mod.group_scale(0.0)).view(np.uint32) == 0x57CBBA10
+    assert np.float32(oracle_mod.group_scale(0.0, True)).view(np.uint32) == 0x57800000
+
+
+# ------------------------------------------------------------- invariants
+
+
+def random_case(seed, M, K, G, axis, sigma=0.02, outliers=True):
+    rng = np.random.default_rng(seed)
+    x = wl.randn_bf16(rng, (M, K), sigma, 0.002 if outliers else 0.0, 8.0)
+    extent = M if axis == 0 else K
+    off = wl.uniform_group_offsets(rng, extent, G)
+    return x, off
+
+
+def check_slices(x_f, q, s_of, slices, pow2):
+    for (idx, s) in slices:
+        xs = x_f[idx].astype(np.float32)
+        v = (xs * np.float32(s)).astype(np.float32)
+        d = DEC[q[idx]]
+        assert np.all(np.abs(d - v.astype(np.float64)) <= half_step(np.minimum(np.abs(v), 448.0)) + 0.0)
+        nz = v != 0
+        assert np.all(np.signbit(d[nz]) == np.signbit(v[nz]))
+        amax = float(np.abs(xs).max()) if xs.size else 0.0
+        if xs.size and amax >= EPS32:
+            m = float(np.abs(d).max())
+            if pow2:
+                assert 224.0 <= m <= 448.0
+            else:
+                assert m == 448.0
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("seed,M,K,G", [(11, 96, 40, 5), (12, 64, 24, 1), (13, 160, 8, 9)])
+def test_dim0_invariants(oracle_mod, seed, M, K, G, pow2):
+    x, off = random_case(seed, M, K, G, 0)
+    q, s = oracle_mod.quant_groups_dim0(x, off, pow2)
+    xf = wl.bf16_bits_to_f32(x)
+    starts = np.concatenate([[0], off[:-1]])
+    slices = []
+    for g in range(G):
+        for k in range(K):
+            slices.append(((slice(starts[g], off[g]), k), s[g, k]))
+            if starts[g] == off[g]:
+                assert s[g, k].view(np.uint32) == (0x57800000 if pow2 else 0x57CBBA10)
+    check_slices(xf, q, None, slices, pow2)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("seed,M,K,G", [(21, 7, 160, 5), (22, 3, 64, 1), (23, 5, 320, 17)])
+def test_dim1_invariants(oracle_mod, seed, M, K, G, pow2):
+    x, off = random_case(seed, M, K, G, 1)
+    q, s = oracle_mod.quant_groups_dim1(x, off, pow2)
+    xf = wl.bf16_bits_to_f32(x)
+    starts = np.concatenate([[0], off[:-1]])
+    slices = [((r, slice(starts[g], off[g])), s[r, g]) for r in range(M) for g in range(G)]
+    check_slices(xf, q, None, slices, pow2)
+
+
+# ------------------------------------------------- locality / boundaries
+
+
+def test_dim0_groups_are_independent(oracle_mod):
+    x, off = random_case(31, 128, 32, 6, 0)
+    q0, s0 = oracle_mod.quant_groups_dim0(x, off)
+    starts = np.concatenate([[0], off[:-1]])
+    g = int(np.argmax(off - starts))
+    x2 = x.copy()
+    x2[starts[g]:off[g]] = wl.f32_to_bf16_bits(np.full((off[g] - starts[g], 32), 100.0, np.float32))
+    q1, s1 = oracle_mod.quant_groups_dim0(x2, off)
+    other = np.ones(128, bool)
+    other[starts[g]:off[g]] = False
+    assert np.array_equal(q0[other], q1[other])
+    keep = np.arange(len(off)) != g
+    assert np.array_equal(s0[keep].view(np.uint32), s1[keep].view(np.uint32))
+    assert np.all(q1[starts[g]:off[g]] == 0x7E)
+
+
+def test_dim1_groups_are_independent(oracle_mod):
+    x, off = random_case(32, 4, 256, 6, 1)
+    q0, s0 = oracle_mod.quant_groups_dim1(x, off)
+    starts = np.concatenate([[0], off[:-1]])
+    g = int(np.argmax(off - starts))
+    x2 = x.copy()
+    x2[:, starts[g]:off[g]] = wl.f32_to_bf16_bits(np.full((4, off[g] - starts[g]), -3.0, np.float32))
+    q1, s1 = oracle_mod.quant_groups_dim1(x2, off)
+    other = np.ones(256, bool)
+    other[starts[g]:off[g]] = False
+    assert np.array_equal(q0[:, other], q1[:, other])
+    keep = np.arange(len(off)) != g
+    assert np.array_equal(s0[:, keep].view(np.uint32), s1[:, keep].view(np.uint32))
+    assert np.all(q1[:, starts[g]:off[g]] == 0xFE)
+
+
+# ---------------------------------------------------- transpose identity
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_transpose_identity(oracle_mod, pow2):
+    """Per-group rowwise scales of T^T equal per-group colwise scales of T,
+    transposed (the rowwise page's Summary: the transpose method)."""
+    x, off = random_case(41, 208, 48, 7, 0)
+    q0, s0 = oracle_mod.quant_groups_dim0(x, off, pow2)
+    q1, s1 = oracle_mod.quant_groups_dim1(np.ascontiguousarray(x.T), off, pow2)
+    assert np.array_equal(q1, q0.T)
+    assert np.array_equal(s1.view(np.uint32), s0.T.view(np.uint32))
+
+
+def test_bad_offsets_rejected(oracle_mod):
+    x = np.zeros((32, 16), np.uint16)
+    for off in ([16, 8, 32], [16, 31], [33], [-1, 32]):
+        with pytest.raises(ValueError):
+            oracle_mod.quant_groups_dim0(x, np.array(off, np.int32))
+
+
+def test_dim0_double_rounding_golden(oracle_mod):
+    """fl32(x * s) is rounded to binary32 before the E4M3 cast."""
+    g = golden_io.load()["dim0_double_rounding"]
+    x = np.array([[golden_io.bf16_bits(v) for v in r] for r in g["x"]], np.uint16)
+    q, s = oracle_mod.quant_groups_dim0(x, np.array(g["offsets"], np.int32))
+    assert np.array_equal(s.view(np.uint32), golden_io.hex_matrix_u32(g["scales"]))
+    assert np.array_equal(q, golden_io.hex_matrix_u8(g["q"]))
