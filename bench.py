@@ -1,0 +1,281 @@
+"""Benchmark of the per-group fp8 scale + cast hot path on one MI355X.
+
+A step is one pass of the hot path over the (16640, 8192) bf16 token-major
+gradient with 64 token groups: the colwise per-group cast of T (groups along
+dim0, the operand quantised per (group, column)) followed by the rowwise
+per-group cast of T transposed, (8192, 16640) with groups along dim1. These
+are the two halves of the shape the rowwise page benchmarks ("[moe fp8
+training] test and bench new faster method for per group rowwise scaling",
+Benchmarks table, (16640, 8192) with 64 groups).
+
+The single JSON line on stdout keeps the driver's contract: `value` is the
+algorithmic HBM throughput of the whole step (read bf16 once, write E4M3
+once, write fp32 scales, read offsets) over the timed steps, with every input
+already resident in HBM. `roofline` reports the slower of the two kernels
+against MI355X's 8 TB/s, timed with HIP events on the stream the library
+launches on. `cpu_baseline` times the CPU oracle on a bounded sample of the
+same step. Per-config kernel times (each run after a cache flush) go into
+`kernels`. Human-readable detail goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("mgs_device.hpp", "mgs_kernels.hpp", "mgs_dim0.hip", "mgs_dim1.hip",
+                  "mgs_mx.hip", "mgs_api.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "group_scaling_fp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-config table")
+    ap.add_argument("--cpu-cols", type=int, default=8192,
+                    help="columns of T (and rows of T^T) in the oracle's timed sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the per-group cast needs no cross-GPU exchange, and "
+              "multi-GPU runs are not part of this build (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import group_scaling_fp8_amd as mgs
+    from group_scaling_fp8_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mgs.lib()
+
+    log("generating the (16640, 8192) bf16 workload ...")
+    T = wl.token_major_gradient()
+    off = wl.target_offsets(64)
+    Tt = np.ascontiguousarray(T.T)
+    M, K = T.shape
+    G = len(off)
+    x0 = torch.from_numpy(T.view(np.int16)).to(dev)
+    x1 = torch.from_numpy(Tt.view(np.int16)).to(dev)
+    o = torch.from_numpy(off).to(dev)
+    q0 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s0 = torch.empty((G, K), dtype=torch.float32, device=dev)
+    q1 = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((K, G), dtype=torch.float32, device=dev)
+    bytes_dim0 = wl.Workload("", "dim0", T, off).algorithmic_bytes()
+    bytes_dim1 = wl.Workload("", "dim1", Tt, off).algorithmic_bytes()
+    step_bytes = bytes_dim0 + bytes_dim1
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mgs.mgs_quant_groups_dim0(x0, o, False, q=q0, scales=s0)
+        if ev is not None:
+            ev[1].record(stream)
+        mgs.mgs_quant_groups_dim1(x1, o, False, q=q1, scales=s1)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    d0 = [e[0].elapsed_time(e[1]) for e in evs]
+    d1 = [e[1].elapsed_time(e[2]) for e in evs]
+    avg0, avg1 = float(np.mean(d0)), float(np.mean(d1))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log("step: %.1f us (dim0 %.1f us, dim1 %.1f us by events), %.0f GB/s"
+        % (ms_per_step * 1e3, avg0 * 1e3, avg1 * 1e3, value))
+
+    dominant = "dim0_main_kernel" if avg0 >= avg1 else "dim1_kernel"
+    dom_ms, dom_bytes = (avg0, bytes_dim0) if avg0 >= avg1 else (avg1, bytes_dim1)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dominant), "kernel": dominant,
+                "kernel_us": round(dom_ms * 1e3, 2), "algorithmic_bytes": dom_bytes}
+
+    # parity spot check of this run's outputs on one strip / a few rows
+    import oracle
+    cols = np.arange(0, 128)
+    rq, rs = oracle.quant_groups_dim0(np.ascontiguousarray(T[:, cols]), off)
+    ok0 = (np.array_equal(q0[:, :128].cpu().numpy(), rq)
+           and np.array_equal(s0[:, :128].cpu().numpy().view(np.uint32), rs.view(np.uint32)))
+    rows = np.array([0, 4097, K - 1])
+    rq1, rs1 = oracle.quant_groups_dim1(np.ascontiguousarray(Tt[rows]), off)
+    ok1 = (np.array_equal(q1[rows].cpu().numpy(), rq1)
+           and np.array_equal(s1[rows].cpu().numpy().view(np.uint32), rs1.view(np.uint32)))
+
+    kernels = None
+    if not args.no_kernels:
+        kernels = per_config_table(torch, mgs, wl, dev, T, Tt)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(T, Tt, off, args.cpu_cols)
+
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) per-group fp8 scale+cast, (16640,8192) bf16 G=64",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "per-group fp8 scale+cast of a (16640, 8192) bf16 token-major "
+                               "gradient, G=64: dim0 on T then dim1 on T^T (8192, 16640)",
+                   "M": M, "K": K, "groups": G, "in": "bf16", "out": "e4m3 + fp32 scales",
+                   "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+                   "parity_spot_check": bool(ok0 and ok1),
+                   "device": torch.cuda.get_device_name(0)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def timed_us(torch, fn, flush, reps=20):
+    """Median and min of `reps` single launches, each after a cache flush."""
+    st = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        fn()
+        b.record(st)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return float(np.median(ts)), float(np.min(ts))
+
+
+def per_config_table(torch, mgs, wl, dev, T, Tt):
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    rows = []
+
+    def add(name, kind, x, off, bytes_, fn_maker):
+        fn = fn_maker()
+        fn()
+        torch.cuda.synchronize()
+        med, mn = timed_us(torch, fn, flush)
+        rows.append({"config": name, "kind": kind, "us_median": round(med, 2), "us_min": round(mn, 2),
+                     "algorithmic_GBps": round(bytes_ / (med * 1e-6) / 1e9, 1),
+                     "pct_hbm_peak": round(100 * bytes_ / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2)})
+        log("  %-44s %9.2f us  %7.1f GB/s" % (name, med, rows[-1]["algorithmic_GBps"]))
+
+    def grouped(w):
+        x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+        o = torch.from_numpy(w.offsets).to(dev)
+        f = mgs.mgs_quant_groups_dim0 if w.kind == "dim0" else mgs.mgs_quant_groups_dim1
+        q, s = f(x, o, w.pow2)
+        return lambda: (lambda: f(x, o, w.pow2, q=q, scales=s))
+
+    log("per-config kernel times (cache flushed before each launch):")
+    for w in (wl.c1_dim0_small(), wl.c2_dim0_pow2(), wl.c3_dim0_large(),
+              wl.c6_dim0_target(64, T), wl.c4_dim1(1, T), wl.c4_dim1(16, T), wl.c4_dim1(64, T)):
+        add(w.name, w.kind, w.x, w.offsets, w.algorithmic_bytes(), grouped(w))
+        del w
+    c5 = wl.c5_mx()
+    x5 = torch.from_numpy(c5.x.view(np.int16)).to(dev)
+    for mode, nm in ((mgs.MGS_MX_FLOOR, "FLOOR"), (mgs.MGS_MX_RCEIL, "RCEIL")):
+        q, s = mgs.mgs_mx_quant_dim0(x5, mode)
+        add(c5.name + " " + nm, "mx", c5.x, None, c5.algorithmic_bytes(),
+            lambda: (lambda: mgs.mgs_mx_quant_dim0(x5, mode, q=q, scales=s)))
+    # calibration: plain copy of the same byte count as the target's bf16 input
+    src = torch.empty(T.size * 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    add("copy kernel, %d MiB read + write" % (src.numel() >> 20), "copy", None, None,
+        2 * src.numel(), lambda: (lambda: mgs.mgs_copy(src, dst)))
+    del x5, src, dst, flush
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(T, Tt, off, ncols):
+    """The CPU oracle, untuned and single-threaded, on a bounded sample of
+    the step: dim0 on T[:, :ncols] (every row, every group) and dim1 on the
+    first ncols rows of T^T. Throughput uses the same algorithmic bytes."""
+    import oracle
+    from group_scaling_fp8_amd import workloads as wl
+    xs0 = np.ascontiguousarray(T[:, :ncols])
+    xs1 = np.ascontiguousarray(Tt[:ncols])
+    b = (wl.Workload("", "dim0", xs0, off).algorithmic_bytes()
+         + wl.Workload("", "dim1", xs1, off).algorithmic_bytes())
+    t0 = time.perf_counter()
+    oracle.quant_groups_dim0(xs0, off)
+    oracle.quant_groups_dim1(xs1, off)
+    dt = time.perf_counter() - t0
+    gbps = b / dt / 1e9
+    log("cpu oracle: %.2f s on the sample, %.3f GB/s" % (dt, gbps))
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "dim0 on T[:, :%d] + dim1 on T^T[:%d] (%.1f%% of a step), %.2f s; host: %s, %d cpus"
+                      % (ncols, ncols, 100.0 * ncols / T.shape[1], dt, cpu_model(), os.cpu_count())}
+
+
+if __name__ == "__main__":
+    main()

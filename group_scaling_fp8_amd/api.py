@@ -1,0 +1,126 @@
+"""Torch-tensor front end of the C entry points (argument marshalling only).
+
+PyTorch supplies device memory and the current HIP stream. Inputs must
+already be on the GPU; bf16 tensors may be torch.bfloat16, int16 or
+uint16 (the raw bit patterns are used). Outputs come back as torch.uint8
+(E4M3 bytes; ``.view(torch.float8_e4m3fn)`` reinterprets them), float32
+scales, and uint8 E8M0 scales.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import MGS_FLAG_POW2_SCALE, MGS_MX_FLOOR, MGS_MX_RCEIL, check, lib
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims" % (name, ndim))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, name, (dtype,) if dtype != torch.uint8 else (torch.uint8, torch.float8_e4m3fn))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t
+
+
+def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
+                          q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-group scaling along dim0: x (M, K) bf16, int32 end offsets over M.
+    Returns q (M, K) uint8 E4M3 and scales (G, K) float32."""
+    _need(x, "x", _BF16_LIKE, 2)
+    _need(offsets, "offsets", (torch.int32,), 1)
+    M, K = x.shape
+    G = offsets.shape[0]
+    q = _out(q, (M, K), torch.uint8, x.device, "q")
+    scales = _out(scales, (G, K), torch.float32, x.device, "scales")
+    st = lib().mgs_quant_groups_dim0(x.data_ptr(), M, K, offsets.data_ptr(), G,
+                                     MGS_FLAG_POW2_SCALE if pow2 else 0, q.data_ptr(),
+                                     scales.data_ptr(), _stream_handle(stream))
+    check("mgs_quant_groups_dim0", st)
+    return q, scales
+
+
+def mgs_quant_groups_dim1(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
+                          q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-group rowwise scaling: x (M, K) bf16, int32 end offsets over K
+    (multiples of 16). Returns q (M, K) uint8 E4M3 and scales (M, G) float32."""
+    _need(x, "x", _BF16_LIKE, 2)
+    _need(offsets, "offsets", (torch.int32,), 1)
+    M, K = x.shape
+    G = offsets.shape[0]
+    q = _out(q, (M, K), torch.uint8, x.device, "q")
+    scales = _out(scales, (M, G), torch.float32, x.device, "scales")
+    st = lib().mgs_quant_groups_dim1(x.data_ptr(), M, K, offsets.data_ptr(), G,
+                                     MGS_FLAG_POW2_SCALE if pow2 else 0, q.data_ptr(),
+                                     scales.data_ptr(), _stream_handle(stream))
+    check("mgs_quant_groups_dim1", st)
+    return q, scales
+
+
+def mgs_mx_quant_dim0(x: torch.Tensor, mode: int = MGS_MX_FLOOR,
+                      q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                      offsets: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MX block-32 cast along the last dim: x (M, K) bf16, K % 32 == 0.
+    mode MGS_MX_FLOOR (0) or MGS_MX_RCEIL (1). Returns q (M, K) uint8 E4M3
+    and scales (M, K/32) uint8 E8M0."""
+    _need(x, "x", _BF16_LIKE, 2)
+    if mode not in (MGS_MX_FLOOR, MGS_MX_RCEIL):
+        raise ValueError("mode must be MGS_MX_FLOOR or MGS_MX_RCEIL")
+    M, K = x.shape
+    q = _out(q, (M, K), torch.uint8, x.device, "q")
+    scales = _out(scales, (M, K // 32), torch.uint8, x.device, "scales")
+    off_ptr, G = (None, 0)
+    if offsets is not None:
+        _need(offsets, "offsets", (torch.int32,), 1)
+        off_ptr, G = offsets.data_ptr(), offsets.shape[0]
+    st = lib().mgs_mx_quant_dim0(x.data_ptr(), M, K, off_ptr, G, int(mode), q.data_ptr(),
+                                 scales.data_ptr(), _stream_handle(stream))
+    check("mgs_mx_quant_dim0", st)
+    return q, scales
+
+
+def mgs_cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """E4M3 cast of a float32 tensor (numel % 4 == 0) with the library's cast."""
+    _need(x, "x", (torch.float32,))
+    out = _out(out, tuple(x.shape), torch.uint8, x.device, "out")
+    st = lib().mgs_cast_e4m3(x.data_ptr(), x.numel(), out.data_ptr(), _stream_handle(stream))
+    check("mgs_cast_e4m3", st)
+    return out
+
+
+def mgs_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """Plain copy kernel (byte size % 16 == 0), for traffic calibration."""
+    if src.device.type != "cuda" or dst.device.type != "cuda":
+        raise ValueError("mgs_copy needs GPU tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("mgs_copy needs contiguous tensors of equal byte size")
+    st = lib().mgs_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream))
+    check("mgs_copy", st)
+    return dst

@@ -1,0 +1,157 @@
+// mgs_api.hip — the C ABI of libmgs.so (declared in include/mgs.h): host-side
+// argument checks, the dim0 workspace, and stream-ordered launches.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "mgs.h"
+#include "mgs_kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MGS_OK;
+    g_last_hip_error = (int)e;
+    return MGS_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Device workspace for the tall-group column partials of dim0, one buffer
+// per (device, stream) so concurrent streams never share it. Buffers grow on
+// demand and live until process exit.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace>* g_ws = nullptr;
+
+hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
+    Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // earlier work on this stream may still read the old buffer
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return e;
+            e = hipFree(w.ptr);
+            if (e != hipSuccess) return e;
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        e = hipMalloc(&w.ptr, bytes);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return hipSuccess;
+}
+
+int check_grouped(const void* x, int64_t M, int64_t K, const int32_t* offsets, int32_t n_groups,
+                  uint32_t flags, const void* q, const float* scales) {
+    if (M < 0 || K < 0) return MGS_ERR_INVALID_ARG;
+    if (n_groups < 1) return MGS_ERR_INVALID_ARG;
+    if (n_groups > MGS_MAX_GROUPS) return MGS_ERR_UNSUPPORTED;
+    if (flags & ~MGS_FLAG_POW2_SCALE) return MGS_ERR_INVALID_ARG;
+    if (!offsets || !aligned(offsets, 4)) return MGS_ERR_INVALID_ARG;
+    if (M > INT32_MAX || K > INT32_MAX) return MGS_ERR_UNSUPPORTED;  // offsets are int32
+    if (M * K > 0) {
+        if (!x || !q || !aligned(x, 16) || !aligned(q, 8)) return MGS_ERR_INVALID_ARG;
+    }
+    (void)scales;
+    return MGS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                          int32_t n_groups, uint32_t flags, void* q, float* scales,
+                          void* stream) {
+    int st = check_grouped(x, M, K, offsets, n_groups, flags, q, scales);
+    if (st != MGS_OK) return st;
+    if (K % 8 != 0) return MGS_ERR_INVALID_ARG;
+    if (K == 0) return MGS_OK;
+    if (!scales || !aligned(scales, 16)) return MGS_ERR_INVALID_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t tall = mgs::dim0_tall_chunk_bound(M, n_groups);
+    void* ws = nullptr;
+    if (tall > 0) {
+        hipError_t e = workspace(s, (size_t)tall * (size_t)K * sizeof(uint32_t), &ws);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, K, offsets,
+                                       n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
+                                       static_cast<uint8_t*>(q), scales,
+                                       static_cast<uint32_t*>(ws), tall, s));
+}
+
+int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                          int32_t n_groups, uint32_t flags, void* q, float* scales,
+                          void* stream) {
+    int st = check_grouped(x, M, K, offsets, n_groups, flags, q, scales);
+    if (st != MGS_OK) return st;
+    if (K % 16 != 0) return MGS_ERR_INVALID_ARG;
+    if (M == 0 || K == 0) return MGS_OK;
+    if (!scales || !aligned(scales, 4)) return MGS_ERR_INVALID_ARG;
+    return hip_status(mgs::launch_dim1(static_cast<const uint16_t*>(x), M, (int)K, offsets,
+                                       n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
+                                       static_cast<uint8_t*>(q), scales,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mgs_mx_quant_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                      int32_t n_groups, int mode, void* q, uint8_t* scales_e8m0, void* stream) {
+    (void)offsets;
+    (void)n_groups;
+    if (M < 0 || K < 0 || K % 32 != 0) return MGS_ERR_INVALID_ARG;
+    if (mode != MGS_MX_FLOOR && mode != MGS_MX_RCEIL) return MGS_ERR_INVALID_ARG;
+    if (M == 0 || K == 0) return MGS_OK;
+    if (M > INT64_MAX / K) return MGS_ERR_UNSUPPORTED;
+    if (!x || !q || !scales_e8m0 || !aligned(x, 16) || !aligned(q, 8)) return MGS_ERR_INVALID_ARG;
+    return hip_status(mgs::launch_mx(static_cast<const uint16_t*>(x), M * K, mode == MGS_MX_RCEIL,
+                                     static_cast<uint8_t*>(q), scales_e8m0,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mgs_cast_e4m3(const float* in, int64_t n, uint8_t* out, void* stream) {
+    if (n < 0 || n % 4 != 0) return MGS_ERR_INVALID_ARG;
+    if (n == 0) return MGS_OK;
+    if (!in || !out || !aligned(in, 16) || !aligned(out, 4)) return MGS_ERR_INVALID_ARG;
+    return hip_status(mgs::launch_cast(in, n, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mgs_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return MGS_ERR_INVALID_ARG;
+    if (bytes == 0) return MGS_OK;
+    if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MGS_ERR_INVALID_ARG;
+    return hip_status(mgs::launch_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* mgs_status_string(int status) {
+    switch (status) {
+        case MGS_OK: return "ok";
+        case MGS_ERR_INVALID_ARG: return "invalid argument";
+        case MGS_ERR_UNSUPPORTED: return "unsupported";
+        case MGS_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int mgs_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

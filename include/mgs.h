@@ -1,0 +1,149 @@
+/*
+ * mgs.h — MI355X (gfx950) per-group fp8 scaling: C ABI of libmgs.so.
+ *
+ * The method (page titles, then the part of the page that defines it):
+ *   [ROWWISE]   "[moe fp8 training] test and bench new faster method for per
+ *               group rowwise scaling" — Summary: per-group rowwise scales of
+ *               the backward's grouped GEMM operand, and the transpose
+ *               identity between rowwise and colwise per-group scaling.
+ *   [BLOCKSIZE] "[moe training] use smaller block sizes for per group scaling
+ *               kernels to improve perf" — description: per-token-group
+ *               scaling along dim0; torch.compile failure report: kernel
+ *               argument dict (fp8_dtype_min -448, fp8_dtype_max 448,
+ *               EPS 1e-12, round_scales_to_power_of_2, in-place output) and
+ *               the token-group alignment of 16 in its test source.
+ *   [MXA2A]     "[mxfp8 moe training] fix mxfp8 a2a bench script; set mxfp8
+ *               a2a scaling type to RCEIL" — Summary and investigation
+ *               comment: the mxfp8 dim0 cast, FLOOR and RCEIL scaling.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major
+ *     arrays owned by the caller; outputs are fully overwritten in place.
+ *     bf16 inputs are raw 16-bit patterns (upper halves of binary32).
+ *   - `offsets` are int32 END offsets in device memory: group g covers
+ *     [off[g-1], off[g]) with off[-1] = 0. They must be non-decreasing and
+ *     off[n_groups-1] must equal the grouped extent. They are not checked on
+ *     the host (that would need a device sync). The kernels clamp them into
+ *     range, so bad offsets give wrong values but no out-of-bounds access.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
+ *     asynchronous and stream-ordered. Calls are thread-safe.
+ *   - Return value: an mgs_status. Argument errors are reported before any
+ *     GPU work is queued. MGS_ERR_HIP reports a failed launch or allocation.
+ *   - Numerics: scale = fl32(448 / max(amax, 1e-12)) with one IEEE binary32
+ *     division. With MGS_FLAG_POW2_SCALE it is rounded down to a power of
+ *     two. q = E4M3(fl32(x * scale)): clamp to [-448, 448], round to
+ *     nearest with ties to even (OCP OFP8 E4M3, 0x7E = 448). Subnormals are
+ *     preserved, and the sign of zero is kept.
+ *   - Inputs must be finite (no NaN or Inf); non-finite inputs are outside
+ *     the contract.
+ */
+#ifndef MGS_H
+#define MGS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MGS_OK = 0,
+    MGS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, alignment, flag or mode */
+    MGS_ERR_UNSUPPORTED = 2,   /* valid but beyond this library's limits */
+    MGS_ERR_HIP = 3            /* a HIP launch or allocation failed */
+} mgs_status;
+
+#define MGS_FLAG_POW2_SCALE 1u /* round scales down to a power of two */
+
+enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
+
+#define MGS_MAX_GROUPS 1024    /* n_groups limit of the grouped entry points */
+
+/*
+ * Per-group scaling along dim0 ([BLOCKSIZE] description; constants from the
+ * kernel-argument dict of its torch.compile failure report).
+ *   x       (M, K) bf16. Groups split the M rows.
+ *   offsets n_groups int32 end offsets along M, 1 <= n_groups <= 1024.
+ *   flags   0 or MGS_FLAG_POW2_SCALE.
+ *   q       (M, K) E4M3 bytes, written.
+ *   scales  (n_groups, K) fp32, written. scales[g, k] is the multiplier for
+ *           column k of group g. An empty group still gets its row, with the
+ *           value for amax = 0 (0x57CBBA10, or 0x57800000 with pow2).
+ * Requirements: M >= 0, K >= 0, K % 8 == 0; x 16-byte aligned, q 8-byte
+ * aligned, scales 16-byte aligned. M == 0 writes only the scales; K == 0 is a
+ * no-op.
+ * Memory: groups taller than 512 rows are split into chunks whose column
+ * maxima go through a device workspace. The library allocates it once per
+ * (device, stream) with hipMalloc, grows it as needed, and frees it only at
+ * process exit. The first call that needs more workspace allocates, so that
+ * call is not graph-capture safe.
+ */
+int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
+                          const int32_t *offsets, int32_t n_groups,
+                          uint32_t flags, void *q, float *scales,
+                          void *stream);
+
+/*
+ * Per-group rowwise scaling along dim1 ([ROWWISE] Summary).
+ *   x       (M, K) bf16. Groups split the K columns.
+ *   offsets n_groups int32 end offsets along K. Every offset must be a
+ *           multiple of 16 (the token-group alignment of [BLOCKSIZE]'s test
+ *           source), 1 <= n_groups <= 1024.
+ *   flags   0 or MGS_FLAG_POW2_SCALE.
+ *   q       (M, K) E4M3 bytes, written.
+ *   scales  (M, n_groups) fp32, written. Empty groups get the amax = 0 value.
+ * Requirements: K % 16 == 0; x 16-byte aligned, q 8-byte aligned, scales
+ * 4-byte aligned. M == 0 or K == 0 is a no-op.
+ */
+int mgs_quant_groups_dim1(const void *x, int64_t M, int64_t K,
+                          const int32_t *offsets, int32_t n_groups,
+                          uint32_t flags, void *q, float *scales,
+                          void *stream);
+
+/*
+ * MX-style block-32 cast along the last dim ([MXA2A] investigation comment:
+ * the mxfp8 dim0 cast; Summary: RCEIL scaling type).
+ *   x       (M, K) bf16, K % 32 == 0. Each block of 32 consecutive elements
+ *           of a row has amax a. Its exponent e is floor(log2 a) - 8 (FLOOR)
+ *           or the smallest integer with a <= 448 * 2^e (RCEIL). e is
+ *           clamped to [-127, 127], and a == 0 gives -127.
+ *   offsets, n_groups  accepted so that the three calls share a shape. Blocks
+ *           never cross a row, so token groups cannot change the result.
+ *           They are ignored and may be NULL / 0.
+ *   mode    MGS_MX_FLOOR or MGS_MX_RCEIL.
+ *   q       (M, K) E4M3 bytes: E4M3(x * 2^-e), saturating, RNE.
+ *   scales_e8m0  (M, K/32) bytes: e + 127 (OCP MX E8M0).
+ * Requirements: x 16-byte aligned, q 8-byte aligned.
+ */
+int mgs_mx_quant_dim0(const void *x, int64_t M, int64_t K,
+                      const int32_t *offsets, int32_t n_groups, int mode,
+                      void *q, uint8_t *scales_e8m0, void *stream);
+
+/*
+ * The library's own E4M3 cast on its own: out[i] = E4M3(clamp(in[i])), the
+ * last step of every entry point above, exposed so it can be checked over
+ * 2^32 binary32 inputs. in: n fp32 values, out: n bytes (device). +-Inf
+ * saturate to 0x7E / 0xFE; NaN inputs are outside the contract.
+ * Requirements: n % 4 == 0, in 16-byte aligned, out 4-byte aligned.
+ */
+int mgs_cast_e4m3(const float *in, int64_t n, uint8_t *out, void *stream);
+
+/*
+ * A plain device-to-device copy kernel of `bytes` bytes (bytes % 16 == 0,
+ * both pointers 16-byte aligned), used to calibrate HBM traffic counters
+ * against a kernel of known size.
+ */
+int mgs_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+/* Static text for a status code. */
+const char *mgs_status_string(int status);
+
+/* The last HIP error code seen by this library on the calling thread (0 if
+ * none); meaningful after a call returned MGS_ERR_HIP. */
+int mgs_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGS_H */

@@ -64,6 +64,8 @@ def _load():
     lib.oracle_e4m3_encode.restype = ctypes.c_uint8
     lib.oracle_e4m3_encode_array.argtypes = [ctypes.POINTER(ctypes.c_double), i64, u8p]
     lib.oracle_e4m3_encode_array.restype = None
+    lib.oracle_e4m3_encode_f32_bits.argtypes = [ctypes.c_uint32, i64, u8p]
+    lib.oracle_e4m3_encode_f32_bits.restype = None
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_decode.restype = ctypes.c_double
     lib.oracle_group_scale.argtypes = [ctypes.c_float, ctypes.c_int]
@@ -103,6 +105,14 @@ def e4m3_encode_array(v: np.ndarray) -> np.ndarray:
     _load().oracle_e4m3_encode_array(_ptr(flat, ctypes.c_double), flat.size,
                                      _ptr(out, ctypes.c_uint8))
     return out.reshape(np.shape(v))
+
+
+def e4m3_encode_f32_bits(first: int, n: int) -> np.ndarray:
+    """Codes of the binary32 values with bit patterns first .. first+n-1.
+    The C call releases the GIL, so threads can split a large range."""
+    out = np.empty(int(n), dtype=np.uint8)
+    _load().oracle_e4m3_encode_f32_bits(int(first) & 0xFFFFFFFF, int(n), _ptr(out, ctypes.c_uint8))
+    return out
 
 
 def e4m3_decode(code: int) -> float:

@@ -121,6 +121,19 @@ void oracle_e4m3_encode_array(const double *v, int64_t n, uint8_t *out)
     fpenv_leave(env);
 }
 
+void oracle_e4m3_encode_f32_bits(uint32_t first, int64_t n, uint8_t *out)
+{
+    unsigned env = fpenv_enter();
+    int64_t i;
+    for (i = 0; i < n; ++i) {
+        uint32_t w = first + (uint32_t)i;
+        float f;
+        memcpy(&f, &w, sizeof f);
+        out[i] = oracle_e4m3_encode((double)f);
+    }
+    fpenv_leave(env);
+}
+
 /* ---- per-group scaling --------------------------------------------------- */
 
 float oracle_group_scale(float amax, int pow2)

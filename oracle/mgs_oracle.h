@@ -46,6 +46,10 @@ uint8_t oracle_e4m3_encode(double v);
 /* Element-wise oracle_e4m3_encode over n values. */
 void oracle_e4m3_encode_array(const double *v, int64_t n, uint8_t *out);
 
+/* oracle_e4m3_encode of the binary32 values whose bit patterns are
+ * first, first + 1, ..., first + n - 1 (mod 2^32). */
+void oracle_e4m3_encode_f32_bits(uint32_t first, int64_t n, uint8_t *out);
+
 /* Decodes one E4M3 byte to its real value (NaN codes decode to NaN). */
 double oracle_e4m3_decode(uint8_t code);
 

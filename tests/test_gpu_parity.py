@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path against the CPU oracle, byte for byte.
+
+Tolerance is zero: E4M3 bytes, fp32 scale bits and E8M0 bytes must be
+identical. Small workloads are compared whole; the full-size workloads
+(benchmark shapes, same launch configuration) are compared on sampled
+columns (dim0: every output of a column depends only on that column) or
+sampled rows (dim1, MX: rows are independent), for which the oracle runs on
+exactly the sampled slice of the same input bytes.
+Every output buffer carries guard bands that must stay untouched.
+"""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import group_scaling_fp8_amd as mgs
+from group_scaling_fp8_amd import workloads as wl
+from gpu_util import Guarded, assert_same_bytes, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mgs.lib()
+
+
+# ----------------------------------------------------------------- runners
+
+
+def gpu_dim0(x, off, pow2=False):
+    M, K = x.shape
+    G = len(off)
+    gq, gs = Guarded((M, K), torch.uint8), Guarded((G, K), torch.float32)
+    mgs.mgs_quant_groups_dim0(to_dev(x), to_dev(off), pow2, q=gq.view, scales=gs.view)
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    return gq.numpy(), gs.numpy()
+
+
+def gpu_dim1(x, off, pow2=False):
+    M, K = x.shape
+    G = len(off)
+    gq, gs = Guarded((M, K), torch.uint8), Guarded((M, G), torch.float32)
+    mgs.mgs_quant_groups_dim1(to_dev(x), to_dev(off), pow2, q=gq.view, scales=gs.view)
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    return gq.numpy(), gs.numpy()
+
+
+def gpu_mx(x, mode):
+    M, K = x.shape
+    gq, gs = Guarded((M, K), torch.uint8), Guarded((M, K // 32), torch.uint8)
+    mgs.mgs_mx_quant_dim0(to_dev(x), mode, q=gq.view, scales=gs.view)
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    return gq.numpy(), gs.numpy()
+
+
+def check_dim0(x, off, pow2=False, what="dim0"):
+    q, s = gpu_dim0(x, off, pow2)
+    rq, rs = oracle.quant_groups_dim0(x, off, pow2)
+    assert_same_bytes(s, rs, what + " scales")
+    assert_same_bytes(q, rq, what + " q")
+
+
+def check_dim1(x, off, pow2=False, what="dim1"):
+    q, s = gpu_dim1(x, off, pow2)
+    rq, rs = oracle.quant_groups_dim1(x, off, pow2)
+    assert_same_bytes(s, rs, what + " scales")
+    assert_same_bytes(q, rq, what + " q")
+
+
+def check_mx(x, mode, what="mx"):
+    q, s = gpu_mx(x, mode)
+    rq, rs = oracle.mx_quant_dim0(x, mode)
+    assert_same_bytes(s, rs, what + " scales")
+    assert_same_bytes(q, rq, what + " q")
+
+
+# ------------------------------------------------------- the cast, all fp32
+
+
+def test_cast_e4m3_every_binary32():
+    """The library's cast against the oracle encoder on all 2^32 patterns
+    (NaN patterns excluded: outside the contract)."""
+    chunk = 1 << 26
+    inp = torch.empty(chunk, dtype=torch.int32, device="cuda")
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    sub = chunk // 16
+    with cf.ThreadPoolExecutor(16) as pool:
+        for c in range(1 << 32 >> 26):
+            first = c * chunk
+            pat = torch.arange(first, first + chunk, dtype=torch.int64, device="cuda")
+            inp.copy_(torch.where(pat >= (1 << 31), pat - (1 << 32), pat).to(torch.int32))
+            mgs.mgs_cast_e4m3(inp.view(torch.float32), out=out)
+            got = out.cpu().numpy()
+            want = np.concatenate(list(pool.map(lambda i: oracle.e4m3_encode_f32_bits(first + i * sub, sub),
+                                                range(16))))
+            bits = np.arange(first, first + chunk, dtype=np.uint64).astype(np.uint32)
+            nan = ((bits & 0x7F800000) == 0x7F800000) & ((bits & 0x7FFFFF) != 0)
+            bad = np.nonzero((got != want) & ~nan)[0]
+            assert bad.size == 0, ["%08x: got %02x want %02x" % (bits[i], got[i], want[i]) for i in bad[:8]]
+
+
+# ---------------------------------------------------------------- dim0
+
+
+def test_dim0_c1():
+    w = wl.c1_dim0_small()
+    check_dim0(w.x, w.offsets, w.pow2, w.name)
+
+
+def test_dim0_c2_pow2_empty_and_zero_groups():
+    w = wl.c2_dim0_pow2()
+    sizes = wl.sizes_from_offsets(w.offsets)
+    assert (sizes == 0).any()
+    check_dim0(w.x, w.offsets, w.pow2, w.name)
+
+
+def sampled_columns(K, n_strips=3, rng_seed=0):
+    """Whole 128-column strips (first, last, and random ones)."""
+    rng = np.random.default_rng(rng_seed)
+    strips = sorted(set([0, K // 128 - 1] + list(rng.integers(0, K // 128, n_strips))))
+    return np.concatenate([np.arange(s * 128, s * 128 + 128) for s in strips])
+
+
+def check_dim0_sampled(w, cols):
+    q, s = gpu_dim0(w.x, w.offsets, w.pow2)
+    xs = np.ascontiguousarray(w.x[:, cols])
+    rq, rs = oracle.quant_groups_dim0(xs, w.offsets, w.pow2)
+    assert_same_bytes(s[:, cols], rs, w.name + " scales")
+    assert_same_bytes(q[:, cols], rq, w.name + " q")
+
+
+def test_dim0_c3_dirichlet_sampled():
+    w = wl.c3_dim0_large()
+    assert wl.sizes_from_offsets(w.offsets).max() > 512     # exercises tall groups
+    check_dim0_sampled(w, sampled_columns(w.x.shape[1]))
+
+
+@pytest.fixture(scope="module")
+def token_major():
+    return wl.token_major_gradient()
+
+
+def test_dim0_c6_target_sampled(token_major):
+    w = wl.c6_dim0_target(64, token_major)
+    check_dim0_sampled(w, sampled_columns(w.x.shape[1], 4))
+
+
+# ---------------------------------------------------------------- dim1
+
+
+@pytest.mark.parametrize("G", [1, 16, 64])
+def test_dim1_c4_sampled(token_major, G):
+    w = wl.c4_dim1(G, token_major)
+    q, s = gpu_dim1(w.x, w.offsets)
+    rng = np.random.default_rng(G)
+    rows = np.unique(np.concatenate([[0, w.x.shape[0] - 1], rng.integers(0, w.x.shape[0], 96)]))
+    rq, rs = oracle.quant_groups_dim1(np.ascontiguousarray(w.x[rows]), w.offsets)
+    assert_same_bytes(s[rows], rs, w.name + " scales")
+    assert_same_bytes(q[rows], rq, w.name + " q")
+
+
+# ------------------------------------------------------------------ MX
+
+
+@pytest.fixture(scope="module")
+def c5():
+    return wl.c5_mx()
+
+
+@pytest.mark.parametrize("mode", [mgs.MGS_MX_FLOOR, mgs.MGS_MX_RCEIL])
+def test_mx_c5_sampled(c5, mode):
+    q, s = gpu_mx(c5.x, mode)
+    rng = np.random.default_rng(5 + mode)
+    rows = np.unique(np.concatenate([[0, c5.x.shape[0] - 1], rng.integers(0, c5.x.shape[0], 512)]))
+    rq, rs = oracle.mx_quant_dim0(np.ascontiguousarray(c5.x[rows]), mode)
+    assert_same_bytes(s[rows], rs, "mx scales")
+    assert_same_bytes(q[rows], rq, "mx q")
+
+
+# --------------------------------------------------------------- edges
+
+
+def edge_values(rng, shape):
+    """randn mixed with exact zeros, -0.0, bf16 subnormals, tiny and huge
+    magnitudes and outliers."""
+    x = wl.randn_bf16(rng, shape, 0.02, 0.003, 8.0)
+    n = x.size
+    flat = x.reshape(-1)
+    pick = rng.choice(n, size=max(1, n // 20), replace=False)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80,
+                         0x7F7F, 0xFF7F, 0x0400, 0x1000], dtype=np.uint16)
+    flat[pick] = specials[rng.integers(0, len(specials), len(pick))]
+    return x
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("M,K,sizes", [
+    (1, 8, [1]),
+    (40, 200, [0, 17, 0, 23, 0]),                # ragged strip (K % 128 != 0), empty groups
+    (512, 256, [512]),                           # exactly one chunk
+    (513, 136, [513]),                           # just taller than one chunk
+    (1500, 128, [0, 1024, 3, 473]),              # tall group next to tiny ones
+    (2000, 384, [700, 0, 0, 1300]),
+    (96, 64, [32, 32, 32]),
+])
+def test_dim0_edges(M, K, sizes, pow2):
+    rng = np.random.default_rng(M * 7 + K)
+    x = edge_values(rng, (M, K))
+    off = np.cumsum(sizes).astype(np.int32)
+    assert off[-1] == M
+    # a group of all zeros where there is one with rows
+    nz = [i for i, s in enumerate(sizes) if s > 0]
+    if len(nz) > 1:
+        g = nz[-1]
+        x[off[g] - sizes[g]:off[g]] = 0
+    check_dim0(x, off, pow2, "dim0 edge %s" % (sizes,))
+
+
+def test_dim0_no_rows_writes_scales():
+    x = np.zeros((0, 64), np.uint16)
+    off = np.zeros(3, np.int32)
+    q, s = gpu_dim0(x, off)
+    _, rs = oracle.quant_groups_dim0(x, off)
+    assert_same_bytes(s, rs, "dim0 M=0 scales")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("M,K,sizes", [
+    (3, 16, [16]),
+    (5, 160, [0, 16, 0, 144, 0]),
+    (4, 2080 * 8, None),                         # a c4 row with 64 groups
+    (2, 16384, [16] * 1024),                     # the group limit, every group one vector pair
+    (3, 40960, [0, 20480, 20480]),               # rows longer than one register pass
+    (7, 1024, [1024]),
+])
+def test_dim1_edges(M, K, sizes, pow2):
+    rng = np.random.default_rng(M * 13 + K)
+    x = edge_values(rng, (M, K))
+    off = wl.target_offsets(64) if sizes is None else np.cumsum(sizes).astype(np.int32)
+    assert off[-1] == K
+    check_dim1(x, off, pow2, "dim1 edge")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (17, 5120), (2, 4096 + 32)])
+def test_mx_edges(M, K, mode):
+    rng = np.random.default_rng(M + K)
+    x = edge_values(rng, (M, K))
+    x[0, :32] = 0
+    if K >= 64:
+        x[0, 32:64] = rng.integers(0, 0x80, 32).astype(np.uint16)   # subnormal-only block
+    check_mx(x, mode, "mx edge")
+
+
+def test_every_finite_bf16_through_dim1():
+    """Each finite bf16 value x goes through the kernel's cast with a scale
+    fixed by an anchor in the same (row, group): row r = [x_r, anchor_r, 0...]."""
+    b = np.arange(0x10000, dtype=np.uint32)
+    finite = (b & 0x7F80) != 0x7F80
+    xs = b[finite].astype(np.uint16)
+    mags = xs & 0x7FFF
+    for variant in range(3):
+        if variant == 0:
+            anchor = mags.copy()
+        elif variant == 1:      # next power of two (exponent + 1, mantissa 0)
+            anchor = (((mags >> 7) + 1) << 7).astype(np.uint16)
+        else:                   # 1.75 x that power
+            anchor = ((((mags >> 7) + 1) << 7) | 0x60).astype(np.uint16)
+        anchor = np.where(mags == 0, 0x3F80, anchor)
+        ok = (anchor & 0x7F80) != 0x7F80
+        rows = np.zeros((int(ok.sum()), 16), np.uint16)
+        rows[:, 0] = xs[ok]
+        rows[:, 1] = anchor[ok]
+        check_dim1(rows, np.array([16], np.int32), False, "bf16 sweep %d" % variant)
+
+
+# ------------------------------------------------- identities, determinism
+
+
+def test_transpose_identity_on_gpu():
+    rng = np.random.default_rng(99)
+    T = wl.randn_bf16(rng, (1040, 2048), 0.02, 0.001, 8.0)
+    off = wl.uniform_group_offsets(rng, 1040, 9)
+    q0, s0 = gpu_dim0(T, off)
+    q1, s1 = gpu_dim1(np.ascontiguousarray(T.T), off)
+    assert_same_bytes(q1, q0.T.copy(), "dim1(T^T) vs dim0(T)^T q")
+    assert_same_bytes(s1, s0.T.copy(), "dim1(T^T) vs dim0(T)^T scales")
+
+
+def test_repeat_runs_are_bit_identical():
+    rng = np.random.default_rng(8)
+    x = wl.randn_bf16(rng, (8192, 1024), 1.0)
+    xt, ot = to_dev(x), to_dev(np.array([100, 3000, 3000, 8192], np.int32))
+    a = [mgs.mgs_quant_groups_dim0(xt, ot) for _ in range(2)]
+    b = [mgs.mgs_quant_groups_dim1(xt, to_dev(np.array([512, 1024], np.int32))) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(a[0][0], a[1][0]) and torch.equal(a[0][1], a[1][1])
+    assert torch.equal(b[0][0], b[1][0]) and torch.equal(b[0][1], b[1][1])
+
+
+def test_bad_offsets_stay_in_bounds():
+    """Unsorted and out-of-range offsets give unspecified values but must
+    not write outside the outputs."""
+    rng = np.random.default_rng(3)
+    x = wl.randn_bf16(rng, (300, 256), 1.0)
+    for off in ([400, 10, -5, 300], [-1, -1, 7], [1 << 30, 5]):
+        o = np.array(off, np.int32)
+        gpu_dim0(x, o)
+        gpu_dim1(x, o)
