@@ -16,6 +16,7 @@ MGS_FLAG_POW2_SCALE = 1
 MGS_MX_FLOOR = 0
 MGS_MX_RCEIL = 1
 MGS_MAX_GROUPS = 1024
+MGS_DIM1_MAX_K = 131072
 
 EXPORTS = (
     "mgs_quant_groups_dim0", "mgs_quant_groups_dim1", "mgs_mx_quant_dim0", "mgs_cast_e4m3",

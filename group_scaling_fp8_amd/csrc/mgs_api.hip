@@ -77,6 +77,26 @@ int check_grouped(const void* x, int64_t M, int64_t K, const int32_t* offsets, i
 
 }  // namespace
 
+namespace mgs {
+
+// Two 512-thread dim0 workgroups fit on a CU (104 VGPRs, 32 KiB of LDS each).
+int dim0_grid() {
+    static std::mutex mu;
+    static std::map<int, int> per_device;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 512;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = per_device.find(dev);
+    if (it != per_device.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    per_device[dev] = 2 * cus;
+    return 2 * cus;
+}
+
+}  // namespace mgs
+
 extern "C" {
 
 int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
@@ -88,16 +108,16 @@ int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* of
     if (K == 0) return MGS_OK;
     if (!scales || !aligned(scales, 16)) return MGS_ERR_INVALID_ARG;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int64_t tall = mgs::dim0_tall_chunk_bound(M, n_groups);
+    const int64_t chunks = mgs::dim0_huge_chunk_bound(M);
     void* ws = nullptr;
-    if (tall > 0) {
-        hipError_t e = workspace(s, (size_t)tall * (size_t)K * sizeof(uint32_t), &ws);
+    if (chunks > 0) {
+        hipError_t e = workspace(s, (size_t)chunks * (size_t)K * sizeof(uint32_t), &ws);
         if (e != hipSuccess) return hip_status(e);
     }
-    return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, K, offsets,
+    return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, (int)K, offsets,
                                        n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
                                        static_cast<uint8_t*>(q), scales,
-                                       static_cast<uint32_t*>(ws), tall, s));
+                                       static_cast<uint32_t*>(ws), mgs::dim0_grid(), s));
 }
 
 int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* offsets,
@@ -106,6 +126,7 @@ int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* of
     int st = check_grouped(x, M, K, offsets, n_groups, flags, q, scales);
     if (st != MGS_OK) return st;
     if (K % 16 != 0) return MGS_ERR_INVALID_ARG;
+    if (K > MGS_DIM1_MAX_K) return MGS_ERR_UNSUPPORTED;
     if (M == 0 || K == 0) return MGS_OK;
     if (!scales || !aligned(scales, 4)) return MGS_ERR_INVALID_ARG;
     return hip_status(mgs::launch_dim1(static_cast<const uint16_t*>(x), M, (int)K, offsets,

@@ -4,24 +4,31 @@
 // kernels to improve perf", description (per-token-group scaling along dim0:
 // one scale per (group, column)) and its kernel-argument dict (448, 1e-12,
 // power-of-two rounding). That page's fix was filling every compute unit
-// when groups are small; here every (group, 128-column strip) pair is its
-// own workgroup, and tall groups are split into row chunks, so the grid
-// scales with M and K rather than with the group count.
+// when groups are small. Here every workgroup gets a tile of about the same
+// size whatever the group sizes, so the grid scales with M * K and not with
+// the group count.
 //
-// Work decomposition (all decided on the device from the offsets, so the
-// host never reads them):
-//   * A group of at most kChunkRows rows is one chunk. A taller group is cut
-//     into ceil(rows / kChunkRows) near-equal chunks.
-//   * Workgroup item = (chunk, strip of 128 columns). 256 threads: 16 lanes
-//     per row, each lane holding 8 columns (one 16-byte load), 16 rows per
-//     slab, up to 32 slabs held in registers. So a whole chunk (<= 512 rows
-//     x 128 columns, 128 KiB of bf16) is read from HBM exactly once.
-//   * Single-chunk groups: load -> column amax -> scale -> cast from
-//     registers -> store. One pass.
-//   * Multi-chunk groups: a first kernel writes each chunk's column amax to
-//     a workspace; the main kernel combines the group's partials, then
-//     re-reads its chunk and casts. This second read is the only extra
-//     traffic, and only tall groups pay it.
+// Tiling (all decided on the device from the offsets; the host never reads
+// them). A workgroup has 512 threads and holds up to kSlabs 16-byte vectors
+// per thread in registers (160 KiB of bf16). Its tile is R rows of one group
+// times a strip of 8 * tpr columns, with tpr lanes per row:
+//   * class A, R <= 1280 rows: one pass. tpr is the widest power of two in
+//     [16, 128] whose tile still fits (short groups get strips up to 1024
+//     columns wide), or 8 (64-column strips) for groups of 641..1280 rows.
+//     Load -> column amax -> scale -> cast from registers -> store.
+//   * class B, 1280 < R <= 5120: 64-column strips; the first 1280 rows stay in
+//     registers and the rest is read twice (once for the amax, once for the
+//     cast).
+//   * class C, R > 5120: the group is cut into chunks of at most 640 rows
+//     (128-column strips). A first kernel writes every chunk's column amax
+//     to a workspace; the main kernel combines them, then casts its chunk
+//     from registers. The chunk is read twice. That kernel is launched only
+//     when M > 5120.
+// Items are numbered group by group (chunk by chunk, strips fastest inside a
+// group) and the workgroups are persistent: workgroup b takes items b,
+// b + grid, ..., so workgroups that run at the same time read neighbouring
+// strips of the same rows. Every workgroup builds the group plan once, in
+// LDS, so an item costs no global lookup.
 #include "mgs_device.hpp"
 #include "mgs_kernels.hpp"
 
@@ -29,32 +36,69 @@ namespace mgs {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTpr = 16;                   // lanes per row
-constexpr int kRowsPerSlab = kThreads / kTpr;
-constexpr int kSlabs = kDim0Slabs;
-constexpr int kChunkRows = kRowsPerSlab * kSlabs;
-constexpr int kStripCols = kTpr * 8;
-static_assert(kChunkRows == kDim0ChunkRows, "chunk size mismatch");
-static_assert(kStripCols == kDim0StripCols, "strip width mismatch");
+constexpr int kThreads = 512;
+constexpr int kSlabs = kDim0Slabs;                    // vectors per thread
+constexpr int kCap = kThreads * kSlabs;               // vectors per tile
+constexpr int kRowsW64 = kCap / 8;                    // 1280 rows at 64 columns
+constexpr int kRowsW128 = kCap / 16;                  // 640 rows at 128 columns
+static_assert(kRowsW128 == kDim0HugeChunkRows, "chunk size mismatch");
+static_assert(kRowsW64 * 4 == kDim0HugeRows, "huge-group threshold mismatch");
 
-struct Chunk {
-    int g;          // group index, or -1 if the item does not exist
-    int c;          // chunk index within the group
-    int nc;         // chunks in the group
-    int big_base;   // index of the group's first chunk among tall-group chunks
-    int r0, r1;     // rows of this chunk
+enum { kClassA = 0, kClassB = 1, kClassC = 2 };
+
+struct Tile {
+    int g;          // group, or -1 when the item does not exist
+    int cls;        // kClassA / kClassB / kClassC
+    int lt;         // log2 of lanes per row (3..7)
+    int strip;      // column strip index (strip width 8 << lt)
+    int c, nc;      // chunk index and chunk count (class C), else 0 and 1
+    int r0, r1;     // rows of this tile (the chunk for class C)
+    int cbase;      // class C: index of the group's first chunk in the workspace
 };
 
-// One wave walks the group table in tiles of 64 groups and finds chunk
-// `target`, counting all chunks (tall_only = false) or only the chunks of
-// groups taller than kChunkRows (tall_only = true). Offsets are sanitised
-// on the fly: end[g] = min(max(off[0..g]), M), clamped below at 0, so any
-// offsets array gives in-range rows.
-__device__ void find_chunk(const int32_t* __restrict__ off, int G, int M, int target,
-                           bool tall_only, Chunk* out) {
-    const int lane = threadIdx.x & (kWave - 1);
-    int carry_end = 0, carry_cnt = 0, carry_big = 0;
+// Log2 lanes per row for a group of R rows, and its class.
+__device__ __forceinline__ void choose_tiling(int R, int K, int* lt_out, int* cls_out) {
+    int lt, cls;
+    if (R > kDim0HugeRows) {
+        lt = 4;
+        cls = kClassC;
+    } else if (R > kRowsW64) {
+        lt = 3;
+        cls = kClassB;
+    } else if (R > kRowsW128) {
+        lt = 3;
+        cls = kClassA;
+    } else {
+        lt = 7;
+        while (lt > 4 && R * (1 << lt) > kCap) --lt;
+        cls = kClassA;
+    }
+    // no strip wider than needed to cover K
+    while (lt > 3 && (8 << (lt - 1)) >= K) --lt;
+    *lt_out = lt;
+    *cls_out = cls;
+}
+
+// Per-workgroup plan of every group, in LDS: first row, rows, class, log2
+// lanes per row, strip count, chunk count, end of its item range and (class C)
+// index of its first chunk in the workspace. Built once per workgroup by
+// wave 0. Offsets are sanitised on the fly: end[g] = min(max(off[0..g]), M),
+// clamped below at 0, so any offsets array gives in-range rows.
+struct Plan {
+    int start[kMaxGroups];
+    int rows[kMaxGroups];
+    int code[kMaxGroups];     // cls | lt << 4
+    int iend[kMaxGroups];     // inclusive prefix of items, in group order
+    int cbase[kMaxGroups];    // class C: first workspace chunk of the group
+    int total;
+};
+
+// huge_only: count only the class C chunks (the partial-amax kernel's items)
+__device__ void build_plan(const int32_t* __restrict__ off, int G, int M, int K, bool huge_only,
+                           Plan* p) {
+    if (threadIdx.x >= kWave) return;
+    const int lane = threadIdx.x;
+    int carry_end = 0, carry_cnt = 0, carry_chunks = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
         int raw = g < G ? off[g] : M;
@@ -62,210 +106,268 @@ __device__ void find_chunk(const int32_t* __restrict__ off, int G, int M, int ta
         const int end = max(wave_prefix_imax(raw), carry_end);
         int start = __shfl_up(end, 1, kWave);
         if (lane == 0) start = carry_end;
-        const int size = end - start;
-        const int nc = (g < G) ? (size <= kChunkRows ? 1 : (size + kChunkRows - 1) / kChunkRows) : 0;
-        const int nbig = (size > kChunkRows) ? nc : 0;
-        const int cnt = tall_only ? nbig : nc;
+        const int R = end - start;
+        int lt, cls;
+        choose_tiling(R, K, &lt, &cls);
+        const int ns = (K + (8 << lt) - 1) / (8 << lt);
+        const int nc = cls == kClassC ? (R + kRowsW128 - 1) / kRowsW128 : 1;
+        const int chunks_c = (g < G && cls == kClassC) ? nc : 0;
+        int cnt = 0;
+        if (g < G) cnt = huge_only ? chunks_c * ns : nc * ns;
         const int incl = wave_prefix_sum(cnt) + carry_cnt;
-        const int bincl = wave_prefix_sum(nbig) + carry_big;
-        const bool hit = cnt > 0 && target >= incl - cnt && target < incl;
-        if (hit) {
-            const int c = target - (incl - cnt);
-            const int cs = (size + nc - 1) / nc;
-            out->g = g;
-            out->c = c;
-            out->nc = nc;
-            out->big_base = bincl - nbig;
-            out->r0 = min(start + c * cs, end);
-            out->r1 = min(start + (c + 1) * cs, end);
+        const int cincl = wave_prefix_sum(chunks_c) + carry_chunks;
+        if (g < G) {
+            p->start[g] = start;
+            p->rows[g] = R;
+            p->code[g] = cls | (lt << 4);
+            p->iend[g] = incl;
+            p->cbase[g] = cincl - chunks_c;
         }
-        if (__any(hit)) return;
         carry_end = __shfl(end, kWave - 1, kWave);
         carry_cnt = __shfl(incl, kWave - 1, kWave);
-        carry_big = __shfl(bincl, kWave - 1, kWave);
+        carry_chunks = __shfl(cincl, kWave - 1, kWave);
     }
-    if (lane == 0) out->g = -1;
+    if (lane == 0) p->total = carry_cnt;
 }
 
-// Loads the chunk's rows of this lane's 8 columns into registers (zeros for
-// rows past the chunk or columns past K).
-__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ x, int64_t K, int r0,
-                                           int nrows, int ty, int64_t col, bool col_ok,
-                                           uint4 (&v)[kSlabs]) {
-#pragma unroll
-    for (int s = 0; s < kSlabs; ++s) {
-        v[s] = make_uint4(0u, 0u, 0u, 0u);
-        if (s * kRowsPerSlab < nrows) {
-            const int rr = s * kRowsPerSlab + ty;
-            if (rr < nrows && col_ok)
-                v[s] = *reinterpret_cast<const uint4*>(x + (int64_t)(r0 + rr) * K + col);
-        }
+// Tile of item `item` (item < p->total): the group is the first g with
+// iend[g] > item; inside a group items run chunk by chunk, strips fastest.
+__device__ __forceinline__ Tile tile_of(const Plan* p, int G, int K, int item) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (p->iend[mid] > item) hi = mid; else lo = mid + 1;
     }
+    Tile t;
+    const int g = lo;
+    const int code = p->code[g];
+    t.g = g;
+    t.cls = code & 15;
+    t.lt = code >> 4;
+    const int ns = (K + (8 << t.lt) - 1) / (8 << t.lt);
+    const int R = p->rows[g], start = p->start[g];
+    t.nc = t.cls == kClassC ? (R + kRowsW128 - 1) / kRowsW128 : 1;
+    const int local = item - (p->iend[g] - t.nc * ns);
+    t.c = local / ns;
+    t.strip = local - t.c * ns;
+    if (t.cls == kClassC) {
+        const int cs = (R + t.nc - 1) / t.nc;
+        t.r0 = min(start + t.c * cs, start + R);
+        t.r1 = min(start + (t.c + 1) * cs, start + R);
+    } else {
+        t.r0 = start;
+        t.r1 = start + R;
+    }
+    t.cbase = p->cbase[g];
+    return t;
 }
 
-// Per-lane column amax of the chunk held in registers, as four packed pairs
-// of 15-bit magnitudes (lane tx holds columns 8tx..8tx+7).
-__device__ __forceinline__ uint4 lane_column_amax(const uint4 (&v)[kSlabs], int nrows) {
-    uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
-#pragma unroll
-    for (int s = 0; s < kSlabs; ++s) {
-        if (s * kRowsPerSlab < nrows) {
-            m0 = mag_max2(m0, v[s].x);
-            m1 = mag_max2(m1, v[s].y);
-            m2 = mag_max2(m2, v[s].z);
-            m3 = mag_max2(m3, v[s].w);
-        }
-    }
-    return make_uint4(m0, m1, m2, m3);
+__device__ __forceinline__ void max4(uint4& m, const uint4& t) {
+    m.x = mag_max2(m.x, t.x);
+    m.y = mag_max2(m.y, t.y);
+    m.z = mag_max2(m.z, t.z);
+    m.w = mag_max2(m.w, t.w);
 }
 
-// Combines the per-lane values of all lanes that share a column set (same
-// tx, every ty) and returns the result in threads 0..kTpr-1.
-__device__ __forceinline__ uint4 block_column_amax(uint4 m, uint4 (*red)[kTpr]) {
-    // lanes tx, tx+16, tx+32, tx+48 of a wave share columns
-#pragma unroll
-    for (int d = kTpr; d < kWave; d <<= 1) {
+// Column amax over every lane that shares this lane's 8 columns (same
+// tx = lane mod tpr). The result is valid in threads 0..tpr-1.
+__device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red) {
+    for (int d = tpr; d < kWave; d <<= 1) {
         m.x = mag_max2(m.x, __shfl_xor(m.x, d, kWave));
         m.y = mag_max2(m.y, __shfl_xor(m.y, d, kWave));
         m.z = mag_max2(m.z, __shfl_xor(m.z, d, kWave));
         m.w = mag_max2(m.w, __shfl_xor(m.w, d, kWave));
     }
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    if (lane < kTpr) red[wave][lane] = m;
+    red[threadIdx.x] = m;
     __syncthreads();
-    uint4 r = make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x < kTpr) {
+    uint4 a = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < tpr) {
+        const int stride = tpr > kWave ? tpr : kWave;
+        for (int k = threadIdx.x; k < kThreads; k += stride) max4(a, red[k]);
+    }
+    return a;
+}
+
+struct TileGeom {
+    int tpr, tx, ty, rps, col;
+    bool col_ok;
+};
+
+__device__ __forceinline__ TileGeom tile_geom(const Tile& t, int K) {
+    TileGeom q;
+    q.tpr = 1 << t.lt;
+    q.tx = threadIdx.x & (q.tpr - 1);
+    q.ty = threadIdx.x >> t.lt;
+    q.rps = kThreads >> t.lt;
+    q.col = t.strip * (q.tpr * 8) + q.tx * 8;
+    q.col_ok = q.col < K;
+    return q;
+}
+
+// Loads the first nreg rows of the tile into registers (zeros elsewhere).
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t K, int r0, int nreg,
+                                          const TileGeom& q, uint4 (&v)[kSlabs]) {
 #pragma unroll
-        for (int w = 0; w < kThreads / kWave; ++w) {
-            const uint4 t = red[w][threadIdx.x];
-            r.x = mag_max2(r.x, t.x);
-            r.y = mag_max2(r.y, t.y);
-            r.z = mag_max2(r.z, t.z);
-            r.w = mag_max2(r.w, t.w);
+    for (int s = 0; s < kSlabs; ++s) {
+        v[s] = make_uint4(0u, 0u, 0u, 0u);
+        if (s * q.rps < nreg) {
+            const int rr = s * q.rps + q.ty;
+            if (rr < nreg && q.col_ok)
+                v[s] = *reinterpret_cast<const uint4*>(x + (int64_t)(r0 + rr) * K + q.col);
         }
     }
-    return r;
 }
+
+constexpr int kStreamSlabs = 4;     // rows in flight per lane for streamed (class B) rows
 
 }  // namespace
 
-// First pass for groups taller than one chunk: each (tall chunk, strip)
-// writes its 8-per-lane column amax (one uint32 per column) to
-// ws[tall_chunk * K + column].
-__global__ __launch_bounds__(kThreads) void dim0_tall_partials_kernel(
-        const uint16_t* __restrict__ x, int M, int64_t K, const int32_t* __restrict__ off,
-        int G, int n_strips, uint32_t* __restrict__ ws) {
-    __shared__ Chunk info;
-    __shared__ uint4 red[kThreads / kWave][kTpr];
-    const int target = blockIdx.x / n_strips;
-    const int strip = blockIdx.x % n_strips;
-    if (threadIdx.x < kWave) find_chunk(off, G, M, target, true, &info);
+// Class C first pass: column amax of every (chunk, 128-column strip) of the
+// groups taller than kDim0HugeRows, to ws[chunk * K + column]. Persistent:
+// workgroup b takes items b, b + grid, ...; it exits at once when no group
+// is that tall.
+__global__ __launch_bounds__(kThreads) void dim0_huge_partials_kernel(
+        const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
+        uint32_t* __restrict__ ws) {
+    __shared__ Plan plan;
+    __shared__ uint4 red[kThreads];
+    build_plan(off, G, M, K, true, &plan);
     __syncthreads();
-    if (info.g < 0) return;
-    const int tx = threadIdx.x % kTpr, ty = threadIdx.x / kTpr;
-    const int64_t col = (int64_t)strip * kStripCols + tx * 8;
-    const bool col_ok = col < K;
-    const int nrows = info.r1 - info.r0;
-    uint4 v[kSlabs];
-    load_chunk(x, K, info.r0, nrows, ty, col, col_ok, v);
-    const uint4 m = block_column_amax(lane_column_amax(v, nrows), red);
-    if (threadIdx.x < kTpr && col_ok) {
-        uint32_t* dst = ws + (int64_t)(info.big_base + info.c) * K + col;
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(m.x & 0xFFFFu, m.x >> 16, m.y & 0xFFFFu, m.y >> 16);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(m.z & 0xFFFFu, m.z >> 16, m.w & 0xFFFFu, m.w >> 16);
+    for (int item = blockIdx.x; item < plan.total; item += gridDim.x) {
+        const Tile t = tile_of(&plan, G, K, item);
+        const TileGeom q = tile_geom(t, K);
+        const int nrows = t.r1 - t.r0;
+        uint4 v[kSlabs];
+        load_tile(x, K, t.r0, nrows, q, v);
+        uint4 m = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int s = 0; s < kSlabs; ++s)
+            if (s * q.rps < nrows) max4(m, v[s]);
+        m = block_column_amax(m, q.tpr, red);
+        if (threadIdx.x < q.tpr && q.col_ok) {
+            uint32_t* dst = ws + (int64_t)(t.cbase + t.c) * K + q.col;
+            reinterpret_cast<uint4*>(dst)[0] = make_uint4(m.x & 0xFFFFu, m.x >> 16, m.y & 0xFFFFu, m.y >> 16);
+            reinterpret_cast<uint4*>(dst)[1] = make_uint4(m.z & 0xFFFFu, m.z >> 16, m.w & 0xFFFFu, m.w >> 16);
+        }
+        __syncthreads();     // red is reused by the next item
     }
 }
 
-// Main pass: one workgroup per (chunk, strip) of every group, empty groups
-// included (they write their scale row).
+// Main pass, persistent: workgroup b takes items b, b + grid, ... of every
+// group, empty groups included (they write their scale row).
 __global__ __launch_bounds__(kThreads) void dim0_main_kernel(
-        const uint16_t* __restrict__ x, int M, int64_t K, const int32_t* __restrict__ off,
-        int G, int n_strips, int pow2, uint8_t* __restrict__ q, float* __restrict__ scales,
+        const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
+        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales,
         const uint32_t* __restrict__ ws) {
-    __shared__ Chunk info;
-    __shared__ uint4 red[kThreads / kWave][kTpr];
-    __shared__ float s_scale[kTpr][8];
-    const int target = blockIdx.x / n_strips;
-    const int strip = blockIdx.x % n_strips;
-    if (threadIdx.x < kWave) find_chunk(off, G, M, target, false, &info);
+    __shared__ Plan plan;
+    __shared__ uint4 red[kThreads];
+    __shared__ float s_scale[128 * 8];
+    build_plan(off, G, M, K, false, &plan);
     __syncthreads();
-    if (info.g < 0) return;
-    const int tx = threadIdx.x % kTpr, ty = threadIdx.x / kTpr;
-    const int64_t col = (int64_t)strip * kStripCols + tx * 8;
-    const bool col_ok = col < K;
-    const int nrows = info.r1 - info.r0;
-    const bool tall = info.nc > 1;
+    const bool p2 = pow2 != 0;
+    for (int item = blockIdx.x; item < plan.total; item += gridDim.x) {
+        const Tile t = tile_of(&plan, G, K, item);
+        const TileGeom geo = tile_geom(t, K);
+        const int nrows = t.r1 - t.r0;
+        const int nreg = min(nrows, geo.rps * kSlabs);     // rows held in registers
 
-    uint4 v[kSlabs];
-    load_chunk(x, K, info.r0, nrows, ty, col, col_ok, v);
+        uint4 v[kSlabs];
+        load_tile(x, K, t.r0, nreg, geo, v);
 
-    // Column amax: from the registers for a single-chunk group, else from
-    // the tall-group partials (chunks spread over the ty lanes).
-    uint4 m = make_uint4(0u, 0u, 0u, 0u);
-    if (!tall) {
-        m = lane_column_amax(v, nrows);
-    } else if (col_ok) {
-        for (int c = ty; c < info.nc; c += kRowsPerSlab) {
-            const uint4* src = reinterpret_cast<const uint4*>(ws + (int64_t)(info.big_base + c) * K + col);
-            const uint4 a = src[0], b = src[1];
-            m.x = mag_max2(m.x, a.x | (a.y << 16));
-            m.y = mag_max2(m.y, a.z | (a.w << 16));
-            m.z = mag_max2(m.z, b.x | (b.y << 16));
-            m.w = mag_max2(m.w, b.z | (b.w << 16));
-        }
-    }
-    m = block_column_amax(m, red);
-    if (threadIdx.x < kTpr) {
-        const bool p2 = pow2 != 0;
-        float s[8];
-        s[0] = group_scale(m.x & 0xFFFFu, p2);
-        s[1] = group_scale(m.x >> 16, p2);
-        s[2] = group_scale(m.y & 0xFFFFu, p2);
-        s[3] = group_scale(m.y >> 16, p2);
-        s[4] = group_scale(m.z & 0xFFFFu, p2);
-        s[5] = group_scale(m.z >> 16, p2);
-        s[6] = group_scale(m.w & 0xFFFFu, p2);
-        s[7] = group_scale(m.w >> 16, p2);
+        uint4 m = make_uint4(0u, 0u, 0u, 0u);
+        if (t.cls == kClassC) {
+            // column amax of the whole group from the first pass's partials
+            if (geo.col_ok) {
+                for (int c = geo.ty; c < t.nc; c += geo.rps) {
+                    const uint4* src = reinterpret_cast<const uint4*>(ws + (int64_t)(t.cbase + c) * K + geo.col);
+                    const uint4 a = src[0], b = src[1];
+                    max4(m, make_uint4(a.x | (a.y << 16), a.z | (a.w << 16), b.x | (b.y << 16), b.z | (b.w << 16)));
+                }
+            }
+        } else {
+            // class B: rows past the register capacity are streamed for the amax
+            for (int base = nreg; base < nrows; base += kStreamSlabs * geo.rps) {
+                uint4 u[kStreamSlabs];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s_scale[threadIdx.x][i] = s[i];
-        if (col_ok && info.c == 0) {
-            float4* dst = reinterpret_cast<float4*>(scales + (int64_t)info.g * K + col);
-            dst[0] = make_float4(s[0], s[1], s[2], s[3]);
-            dst[1] = make_float4(s[4], s[5], s[6], s[7]);
-        }
-    }
-    __syncthreads();
-    if (!col_ok) return;
-    const float s0 = s_scale[tx][0], s1 = s_scale[tx][1], s2 = s_scale[tx][2], s3 = s_scale[tx][3];
-    const float s4 = s_scale[tx][4], s5 = s_scale[tx][5], s6 = s_scale[tx][6], s7 = s_scale[tx][7];
+                for (int b = 0; b < kStreamSlabs; ++b) {
+                    u[b] = make_uint4(0u, 0u, 0u, 0u);
+                    const int rr = base + b * geo.rps + geo.ty;
+                    if (rr < nrows && geo.col_ok)
+                        u[b] = *reinterpret_cast<const uint4*>(x + (int64_t)(t.r0 + rr) * K + geo.col);
+                }
 #pragma unroll
-    for (int s = 0; s < kSlabs; ++s) {
-        if (s * kRowsPerSlab < nrows) {
-            const int rr = s * kRowsPerSlab + ty;
-            if (rr < nrows) {
-                const uint2 o = cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7);
-                *reinterpret_cast<uint2*>(q + (int64_t)(info.r0 + rr) * K + col) = o;
+                for (int b = 0; b < kStreamSlabs; ++b) max4(m, u[b]);
+            }
+#pragma unroll
+            for (int s = 0; s < kSlabs; ++s)
+                if (s * geo.rps < nreg) max4(m, v[s]);
+        }
+        m = block_column_amax(m, geo.tpr, red);
+
+        if (threadIdx.x < geo.tpr) {
+            float s[8];
+            s[0] = group_scale(m.x & 0xFFFFu, p2);
+            s[1] = group_scale(m.x >> 16, p2);
+            s[2] = group_scale(m.y & 0xFFFFu, p2);
+            s[3] = group_scale(m.y >> 16, p2);
+            s[4] = group_scale(m.z & 0xFFFFu, p2);
+            s[5] = group_scale(m.z >> 16, p2);
+            s[6] = group_scale(m.w & 0xFFFFu, p2);
+            s[7] = group_scale(m.w >> 16, p2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s_scale[threadIdx.x * 8 + i] = s[i];
+            if (geo.col_ok && t.c == 0) {
+                float4* dst = reinterpret_cast<float4*>(scales + (int64_t)t.g * K + geo.col);
+                dst[0] = make_float4(s[0], s[1], s[2], s[3]);
+                dst[1] = make_float4(s[4], s[5], s[6], s[7]);
             }
         }
+        __syncthreads();
+        if (geo.col_ok) {
+            const float* ss = s_scale + geo.tx * 8;
+            const float s0 = ss[0], s1 = ss[1], s2 = ss[2], s3 = ss[3];
+            const float s4 = ss[4], s5 = ss[5], s6 = ss[6], s7 = ss[7];
+#pragma unroll
+            for (int s = 0; s < kSlabs; ++s) {
+                if (s * geo.rps < nreg) {
+                    const int rr = s * geo.rps + geo.ty;
+                    if (rr < nreg)
+                        *reinterpret_cast<uint2*>(q + (int64_t)(t.r0 + rr) * K + geo.col) =
+                            cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7);
+                }
+            }
+            // class B: second read of the streamed rows
+            for (int base = nreg; base < nrows; base += kStreamSlabs * geo.rps) {
+                uint4 u[kStreamSlabs];
+#pragma unroll
+                for (int b = 0; b < kStreamSlabs; ++b) {
+                    u[b] = make_uint4(0u, 0u, 0u, 0u);
+                    const int rr = base + b * geo.rps + geo.ty;
+                    if (rr < nrows) u[b] = *reinterpret_cast<const uint4*>(x + (int64_t)(t.r0 + rr) * K + geo.col);
+                }
+#pragma unroll
+                for (int b = 0; b < kStreamSlabs; ++b) {
+                    const int rr = base + b * geo.rps + geo.ty;
+                    if (rr < nrows)
+                        *reinterpret_cast<uint2*>(q + (int64_t)(t.r0 + rr) * K + geo.col) =
+                            cast8(u[b], s0, s1, s2, s3, s4, s5, s6, s7);
+                }
+            }
+        }
+        __syncthreads();     // s_scale and red are reused by the next item
     }
 }
 
-hipError_t launch_dim0(const uint16_t* x, int M, int64_t K, const int32_t* off, int G, bool pow2,
-                       uint8_t* q, float* scales, uint32_t* ws, int64_t tall_chunk_bound,
-                       hipStream_t stream) {
-    const int n_strips = (int)((K + kStripCols - 1) / kStripCols);
-    if (tall_chunk_bound > 0) {
-        const int64_t blocks = tall_chunk_bound * n_strips;
-        hipLaunchKernelGGL(dim0_tall_partials_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, x, M, K, off, G, n_strips, ws);
+hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, bool pow2,
+                       uint8_t* q, float* scales, uint32_t* ws, int grid, hipStream_t stream) {
+    if (M > kDim0HugeRows) {
+        hipLaunchKernelGGL(dim0_huge_partials_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                           stream, x, M, K, off, G, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t chunks = dim0_chunk_bound(M, G);
-    const int64_t blocks = chunks * n_strips;
-    hipLaunchKernelGGL(dim0_main_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, M,
-                       K, off, G, n_strips, pow2 ? 1 : 0, q, scales, ws);
+    hipLaunchKernelGGL(dim0_main_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, M, K,
+                       off, G, pow2 ? 1 : 0, q, scales, ws);
     return hipGetLastError();
 }
 

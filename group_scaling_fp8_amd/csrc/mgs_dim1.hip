@@ -4,20 +4,27 @@
 // rowwise scaling", Summary: one scale per (row, token group) of a row-major
 // tensor whose token groups run along the contiguous dim. The slow kernel on
 // that page lost its time to uncoalesced accesses; here every access runs
-// along the contiguous dim:
-//   * a workgroup (256 threads) owns whole rows; lane l of wave w holds the
-//     16-byte vectors w*64 + l + 256*j (j < V), so each load instruction
-//     reads 1 KiB of a row contiguously;
-//   * group boundaries are multiples of 16 columns (token-group alignment
-//     16, "[moe training] use smaller block sizes ..." test source), so a
-//     vector never straddles two groups;
-//   * per-(row, group) amax is a segmented reduction: the key
-//     (group << 16) | max|x| of each vector goes through a 64-lane prefix
-//     max (DPP), which never mixes groups because group ids grow along the
-//     row; the last lane of each group segment then does one LDS atomic max;
-//   * the row stays in registers between the amax and the cast (single pass)
-//     whenever it fits in 256 * V * 8 columns. Longer rows are processed in
-//     column chunks and re-read for the cast.
+// along the contiguous dim.
+//   * One workgroup owns one row at a time. It is sized to the row: NT
+//     threads (a multiple of 64, at most 1024) with V 16-byte vectors each,
+//     NT * V * 8 >= K. Lane t holds vectors t + NT*j, so each load
+//     instruction of a wave reads 1 KiB of the row contiguously. Few vectors
+//     per thread and many waves per row keep more bytes in flight than a few
+//     long-running waves would.
+//   * Workgroups are persistent over rows (row = block, block + grid, ...)
+//     and load the next row while the current one is reduced and cast.
+//   * Group boundaries are multiples of 16 columns (token-group alignment 16,
+//     test source in "[moe training] use smaller block sizes for per group
+//     scaling kernels to improve perf"), so a vector never straddles two
+//     groups. A vector -> (group, last-vector-of-group) table is built once
+//     per workgroup in LDS.
+//   * Per-(row, group) amax is a segmented reduction: the key
+//     (group << 16) | max|x| of every vector goes through a 64-lane prefix max
+//     (DPP), which never mixes groups because group ids grow along the row;
+//     the last lane of each group segment in a wave then does one LDS atomic
+//     max.
+//   * Rows longer than NT * V * 8 (K > 32768 with NT = 1024, V = 4) are done
+//     in column chunks; their cast re-reads the row (the only extra traffic).
 #include "mgs_device.hpp"
 #include "mgs_kernels.hpp"
 
@@ -25,10 +32,11 @@ namespace mgs {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr uint32_t kNoGroup = 0x7FFFu;     // vector past the last group end
+constexpr uint32_t kTailBit = 0x8000u;     // last vector of its group
 
 // Group of the vector starting at column col: the first g with end[g] > col,
-// or G if none (columns past the last offset belong to no group).
+// or G if there is none.
 __device__ __forceinline__ int group_of(const int* s_end, int G, int col) {
     int lo = 0, hi = G;
     while (lo < hi) {
@@ -39,17 +47,20 @@ __device__ __forceinline__ int group_of(const int* s_end, int G, int col) {
 }
 
 template <int V>
-__global__ __launch_bounds__(kThreads) void dim1_kernel(
+__global__ __launch_bounds__(1024) void dim1_kernel(
         const uint16_t* __restrict__ x, int64_t M, int K, const int32_t* __restrict__ off, int G,
-        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int rows_per_block) {
+        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales) {
     extern __shared__ int smem[];
-    int* s_end = smem;                                                   // G
-    uint32_t* s_amax = reinterpret_cast<uint32_t*>(smem + G);           // G
-    float* s_scale = reinterpret_cast<float*>(smem + 2 * G);            // G
-
+    const int NT = blockDim.x;
+    const int nvec = K / 8;
+    int* s_end = smem;                                               // G
+    uint32_t* s_amax = reinterpret_cast<uint32_t*>(smem + G);        // G
+    float* s_scale = reinterpret_cast<float*>(smem + 2 * G);         // G
+    uint16_t* vtab = reinterpret_cast<uint16_t*>(smem + 3 * G);      // nvec
     const int lane = threadIdx.x & (kWave - 1);
+
     if (threadIdx.x < kWave) {
-        // sanitised end offsets: running max of the clamped raw values
+        // sanitised end offsets: running max of the raw values clamped to [0, K]
         int carry = 0;
         for (int base = 0; base < G; base += kWave) {
             const int g = base + lane;
@@ -60,96 +71,117 @@ __global__ __launch_bounds__(kThreads) void dim1_kernel(
             carry = __shfl(end, kWave - 1, kWave);
         }
     }
-    for (int t = threadIdx.x; t < G; t += kThreads) s_amax[t] = 0u;
+    for (int t = threadIdx.x; t < G; t += NT) s_amax[t] = 0u;
+    __syncthreads();
+    for (int vi = threadIdx.x; vi < nvec; vi += NT) {
+        const int c = vi * 8;
+        const int g = group_of(s_end, G, c);
+        uint32_t e = kNoGroup;
+        if (g < G) e = (uint32_t)g | ((c + 8 >= s_end[g]) ? kTailBit : 0u);
+        vtab[vi] = (uint16_t)e;
+    }
     __syncthreads();
 
-    const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
-    const int64_t row1 = min(row0 + rows_per_block, M);
-    const int chunk_cols = kThreads * V * 8;
-    const int n_cc = (K + chunk_cols - 1) / chunk_cols;
+    const int chunk_vecs = NT * V;
+    const int n_cc = (nvec + chunk_vecs - 1) / chunk_vecs;
     const bool p2 = pow2 != 0;
 
-    int gid[V];
-    bool tail[V];
+    uint32_t e[V];
     auto map_slots = [&](int cc) {
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            const int col = cc * chunk_cols + (threadIdx.x + j * kThreads) * 8;
-            int g = G;
-            bool t = false;
-            if (col < K) {
-                g = group_of(s_end, G, col);
-                t = (g < G) && (lane == kWave - 1 || col + 8 >= s_end[g]);
-            }
-            gid[j] = g;
-            tail[j] = t;
+            const int vi = cc * chunk_vecs + threadIdx.x + NT * j;
+            e[j] = vi < nvec ? vtab[vi] : kNoGroup;
         }
     };
-    auto load_slots = [&](const uint16_t* xr, int cc, uint4 (&v)[V]) {
+    auto load_slots = [&](int64_t row, int cc, uint4 (&v)[V]) {
+        const uint16_t* xr = x + row * (int64_t)K;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            const int col = cc * chunk_cols + (threadIdx.x + j * kThreads) * 8;
             v[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (gid[j] < G) v[j] = *reinterpret_cast<const uint4*>(xr + col);
+            if ((e[j] & kNoGroup) != kNoGroup) {
+                const int vi = cc * chunk_vecs + threadIdx.x + NT * j;
+                v[j] = *reinterpret_cast<const uint4*>(xr + (int64_t)vi * 8);
+            }
         }
     };
     auto amax_slots = [&](const uint4 (&v)[V]) {
 #pragma unroll
         for (int j = 0; j < V; ++j) {
+            const uint32_t gid = e[j] & kNoGroup;
             uint32_t key = 0u;
-            if (gid[j] < G) key = ((uint32_t)gid[j] << 16) | mag_fold(mag_max8(0u, v[j]));
+            if (gid != kNoGroup) key = (gid << 16) | mag_fold(mag_max8(0u, v[j]));
             key = wave_prefix_max(key);
-            if (tail[j]) atomicMax(&s_amax[gid[j]], key & 0xFFFFu);
+            if (gid != kNoGroup && ((e[j] & kTailBit) || lane == kWave - 1))
+                atomicMax(&s_amax[gid], key & 0xFFFFu);
         }
     };
-    auto cast_slots = [&](uint8_t* qr, int cc, const uint4 (&v)[V]) {
+    auto cast_slots = [&](int64_t row, int cc, const uint4 (&v)[V]) {
+        uint8_t* qr = q + row * (int64_t)K;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            if (gid[j] < G) {
-                const int col = cc * chunk_cols + (threadIdx.x + j * kThreads) * 8;
-                *reinterpret_cast<uint2*>(qr + col) = cast8(v[j], s_scale[gid[j]]);
+            const uint32_t gid = e[j] & kNoGroup;
+            if (gid != kNoGroup) {
+                const int vi = cc * chunk_vecs + threadIdx.x + NT * j;
+                *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = cast8(v[j], s_scale[gid]);
             }
+        }
+    };
+    auto scales_of_row = [&](int64_t row) {
+        for (int g = threadIdx.x; g < G; g += NT) {
+            const float s = group_scale(s_amax[g], p2);
+            s_scale[g] = s;
+            scales[row * G + g] = s;
+            s_amax[g] = 0u;
         }
     };
 
-    uint4 v[V];
-    if (n_cc == 1) map_slots(0);
-    for (int64_t row = row0; row < row1; ++row) {
-        const uint16_t* xr = x + row * (int64_t)K;
-        uint8_t* qr = q + row * (int64_t)K;
-        for (int cc = 0; cc < n_cc; ++cc) {
-            if (n_cc > 1) map_slots(cc);
-            load_slots(xr, cc, v);
+    if (n_cc == 1) {
+        // Whole row in registers; the next row is loaded before this one is
+        // reduced and cast.
+        map_slots(0);
+        uint4 v[V], vn[V];
+        int64_t row = blockIdx.x;
+        if (row < M) load_slots(row, 0, vn);
+        for (; row < M; row += gridDim.x) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) v[j] = vn[j];
+            if (row + gridDim.x < M) load_slots(row + gridDim.x, 0, vn);
             amax_slots(v);
+            __syncthreads();
+            scales_of_row(row);
+            __syncthreads();
+            cast_slots(row, 0, v);
         }
-        __syncthreads();
-        for (int t = threadIdx.x; t < G; t += kThreads) {
-            const float s = group_scale(s_amax[t], p2);
-            s_scale[t] = s;
-            scales[row * G + t] = s;
-            s_amax[t] = 0u;
-        }
-        __syncthreads();
-        for (int cc = 0; cc < n_cc; ++cc) {
-            if (n_cc > 1) {
+    } else {
+        // Long rows: amax over column chunks, then re-read each chunk to cast.
+        uint4 v[V];
+        for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+            for (int cc = 0; cc < n_cc; ++cc) {
                 map_slots(cc);
-                load_slots(xr, cc, v);      // second read of long rows
+                load_slots(row, cc, v);
+                amax_slots(v);
             }
-            cast_slots(qr, cc, v);
+            __syncthreads();
+            scales_of_row(row);
+            __syncthreads();
+            for (int cc = 0; cc < n_cc; ++cc) {
+                map_slots(cc);
+                load_slots(row, cc, v);
+                cast_slots(row, cc, v);
+            }
         }
     }
 }
 
 template <int V>
 hipError_t launch_v(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,
-                    uint8_t* q, float* scales, hipStream_t stream) {
-    // Enough workgroups to fill 256 CUs several times over, a few rows each.
-    int64_t rpb = M / (256 * 8);
-    rpb = rpb < 1 ? 1 : (rpb > 64 ? 64 : rpb);
-    const int64_t blocks = (M + rpb - 1) / rpb;
-    const size_t shmem = (size_t)3 * G * sizeof(int);
-    hipLaunchKernelGGL(dim1_kernel<V>, dim3((unsigned)blocks), dim3(kThreads), shmem, stream, x, M,
-                       K, off, G, pow2 ? 1 : 0, q, scales, (int)rpb);
+                    uint8_t* q, float* scales, int threads, hipStream_t stream) {
+    // about four workgroups per CU, each walking several rows
+    const int64_t blocks = M < 1024 ? M : 1024;
+    const size_t shmem = (size_t)3 * G * sizeof(int) + (size_t)(K / 8) * sizeof(uint16_t) + 16;
+    hipLaunchKernelGGL(dim1_kernel<V>, dim3((unsigned)blocks), dim3(threads), shmem, stream, x, M,
+                       K, off, G, pow2 ? 1 : 0, q, scales);
     return hipGetLastError();
 }
 
@@ -157,14 +189,22 @@ hipError_t launch_v(const uint16_t* x, int64_t M, int K, const int32_t* off, int
 
 hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,
                        uint8_t* q, float* scales, hipStream_t stream) {
-    const int vecs_per_thread = (K / 8 + kThreads - 1) / kThreads;
-    if (vecs_per_thread <= 1) return launch_v<1>(x, M, K, off, G, pow2, q, scales, stream);
-    if (vecs_per_thread <= 2) return launch_v<2>(x, M, K, off, G, pow2, q, scales, stream);
-    if (vecs_per_thread <= 4) return launch_v<4>(x, M, K, off, G, pow2, q, scales, stream);
-    if (vecs_per_thread <= 6) return launch_v<6>(x, M, K, off, G, pow2, q, scales, stream);
-    if (vecs_per_thread <= 9) return launch_v<9>(x, M, K, off, G, pow2, q, scales, stream);
-    if (vecs_per_thread <= 12) return launch_v<12>(x, M, K, off, G, pow2, q, scales, stream);
-    return launch_v<16>(x, M, K, off, G, pow2, q, scales, stream);
+    const int nvec = K / 8;
+    // Smallest V whose workgroup (a multiple of 64 threads) fits in 1024
+    // threads; rows longer than 1024 * 4 vectors use V = 4 in column chunks.
+    for (int v = 1; v <= 4; ++v) {
+        const int threads = ((nvec + v - 1) / v + kWave - 1) / kWave * kWave;
+        if (threads <= 1024 || v == 4) {
+            const int t = threads > 1024 ? 1024 : threads;
+            switch (v) {
+                case 1: return launch_v<1>(x, M, K, off, G, pow2, q, scales, t, stream);
+                case 2: return launch_v<2>(x, M, K, off, G, pow2, q, scales, t, stream);
+                case 3: return launch_v<3>(x, M, K, off, G, pow2, q, scales, t, stream);
+                default: return launch_v<4>(x, M, K, off, G, pow2, q, scales, t, stream);
+            }
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mgs

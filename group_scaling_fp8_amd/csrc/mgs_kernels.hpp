@@ -6,27 +6,26 @@
 
 namespace mgs {
 
-// dim0 tiling: a chunk is up to kDim0ChunkRows rows x kDim0StripCols columns.
-constexpr int kDim0Slabs = 32;
-constexpr int kDim0ChunkRows = 16 * kDim0Slabs;
-constexpr int kDim0StripCols = 128;
+// dim0 tiling: 512-thread workgroups holding kDim0Slabs 16-byte vectors per
+// thread; groups taller than kDim0HugeRows are cut into chunks of at most
+// kDim0HugeChunkRows rows whose column maxima go through a workspace.
+constexpr int kDim0Slabs = 20;
+constexpr int kDim0HugeRows = 5120;
+constexpr int kDim0HugeChunkRows = 640;
 
-// Upper bound on the number of chunks over all groups: a group of s rows
-// has ceil(s / C) <= floor(s / C) + 1 chunks (1 if empty).
-inline int64_t dim0_chunk_bound(int64_t M, int64_t G) { return M / kDim0ChunkRows + G; }
-
-// Upper bound on the chunks of groups taller than one chunk: each such group
-// has s > C rows, so there are at most floor(M / C) of them, and its chunks
-// number at most floor(s / C) + 1.
-inline int64_t dim0_tall_chunk_bound(int64_t M, int64_t G) {
-    const int64_t f = M / kDim0ChunkRows;
-    if (M <= kDim0ChunkRows) return 0;
-    return f + (G < f ? G : f);
+// Upper bound on the chunks of groups taller than kDim0HugeRows: such a group
+// of s rows has ceil(s / 640) <= s / 640 + 1 chunks, and there are at most
+// M / 5121 such groups.
+inline int64_t dim0_huge_chunk_bound(int64_t M) {
+    if (M <= kDim0HugeRows) return 0;
+    return M / kDim0HugeChunkRows + M / (kDim0HugeRows + 1) + 1;
 }
 
-hipError_t launch_dim0(const uint16_t* x, int M, int64_t K, const int32_t* off, int G, bool pow2,
-                       uint8_t* q, float* scales, uint32_t* ws, int64_t tall_chunk_bound,
-                       hipStream_t stream);
+// Persistent grid of the dim0 kernels: two 512-thread workgroups per CU.
+int dim0_grid();
+
+hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, bool pow2,
+                       uint8_t* q, float* scales, uint32_t* ws, int grid, hipStream_t stream);
 
 hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,
                        uint8_t* q, float* scales, hipStream_t stream);

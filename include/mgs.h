@@ -58,6 +58,7 @@ typedef enum {
 enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
 
 #define MGS_MAX_GROUPS 1024    /* n_groups limit of the grouped entry points */
+#define MGS_DIM1_MAX_K 131072  /* row length limit of mgs_quant_groups_dim1 */
 
 /*
  * Per-group scaling along dim0 ([BLOCKSIZE] description; constants from the
@@ -72,11 +73,11 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * Requirements: M >= 0, K >= 0, K % 8 == 0; x 16-byte aligned, q 8-byte
  * aligned, scales 16-byte aligned. M == 0 writes only the scales; K == 0 is a
  * no-op.
- * Memory: groups taller than 512 rows are split into chunks whose column
- * maxima go through a device workspace. The library allocates it once per
- * (device, stream) with hipMalloc, grows it as needed, and frees it only at
- * process exit. The first call that needs more workspace allocates, so that
- * call is not graph-capture safe.
+ * Memory: when M > 5120, groups taller than 5120 rows are cut into chunks
+ * whose column maxima go through a device workspace of about
+ * (M / 568) * K * 4 bytes. The library allocates it once per (device, stream)
+ * with hipMalloc, grows it as needed, and frees it only at process exit. A
+ * call that has to grow it is not graph-capture safe.
  */
 int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
                           const int32_t *offsets, int32_t n_groups,
@@ -92,8 +93,9 @@ int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
  *   flags   0 or MGS_FLAG_POW2_SCALE.
  *   q       (M, K) E4M3 bytes, written.
  *   scales  (M, n_groups) fp32, written. Empty groups get the amax = 0 value.
- * Requirements: K % 16 == 0; x 16-byte aligned, q 8-byte aligned, scales
- * 4-byte aligned. M == 0 or K == 0 is a no-op.
+ * Requirements: K % 16 == 0, K <= MGS_DIM1_MAX_K (else MGS_ERR_UNSUPPORTED);
+ * x 16-byte aligned, q 8-byte aligned, scales 4-byte aligned. M == 0 or
+ * K == 0 is a no-op.
  */
 int mgs_quant_groups_dim1(const void *x, int64_t M, int64_t K,
                           const int32_t *offsets, int32_t n_groups,

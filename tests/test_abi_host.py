@@ -73,6 +73,7 @@ def test_grouped_argument_errors(L, fn):
     else:
         assert call(K=24) == INVALID
         assert call(s=A + 2) == INVALID
+        assert call(K=mgs._lib.MGS_DIM1_MAX_K + 16) == UNSUPPORTED
 
 
 def test_mx_argument_errors(L):
