@@ -80,10 +80,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-config table")
+    ap.add_argument("--counter-run", type=int, default=0, metavar="REPS",
+                    help="only launch each hot kernel (and a 256 MiB calibration copy) REPS times, "
+                         "for rocprofv3 counter collection")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="print a markdown summary of rocprofv3 output under DIR (trace/, fetch/, "
+                         "write/ from the commands in profiles/README.md) and write "
+                         "profiles/hbm_traffic.json; needs no GPU")
     ap.add_argument("--cpu-cols", type=int, default=8192,
                     help="columns of T (and rows of T^T) in the oracle's timed sample")
     args = ap.parse_args()
 
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the per-group cast needs no cross-GPU exchange, and "
               "multi-GPU runs are not part of this build (got --gpus %d)" % args.gpus,
@@ -97,6 +107,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mgs.lib()
+    if args.counter_run:
+        counter_run(torch, mgs, wl, dev, args.counter_run)
+        return
 
     log("generating the (16640, 8192) bf16 workload ...")
     T = wl.token_major_gradient()
@@ -131,21 +144,31 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Pass 1 (the contract's timed region): K steps, no event markers between
+    # kernels, bracketed by device synchronisation.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # Pass 2: the same K steps with HIP events around every library call, on
+    # the stream the library launches on, for the per-kernel durations.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     d0 = [e[0].elapsed_time(e[1]) for e in evs]
     d1 = [e[1].elapsed_time(e[2]) for e in evs]
     avg0, avg1 = float(np.mean(d0)), float(np.mean(d1))
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log("step: %.1f us (dim0 %.1f us, dim1 %.1f us by events), %.0f GB/s"
+    log("step: %.1f us; with events: dim0 %.1f us, dim1 %.1f us; %.0f GB/s"
         % (ms_per_step * 1e3, avg0 * 1e3, avg1 * 1e3, value))
 
+    # the dim0 entry point launches dim0_main_kernel, preceded by
+    # dim0_huge_partials_kernel when M > 5120; its event time covers both
     dominant = "dim0_main_kernel" if avg0 >= avg1 else "dim1_kernel"
     dom_ms, dom_bytes = (avg0, bytes_dim0) if avg0 >= avg1 else (avg1, bytes_dim1)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -197,6 +220,97 @@ def main():
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
+
+
+# kernel-name fragments of the library's kernels, and what each one is
+KERNELS = (("copy_kernel", "copy"), ("dim0_main_kernel", "dim0_main_kernel"),
+           ("dim0_huge_partials_kernel", "dim0_huge_partials_kernel"),
+           ("dim1_kernel", "dim1_kernel"), ("mx_kernel", "mx_kernel"))
+COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
+
+
+def _short(name):
+    for frag, short in KERNELS:
+        if frag in name:
+            return short
+    return None
+
+
+def rocprof_summary(d):
+    import csv
+    out = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    stats = os.path.join(d, "trace", "run_kernel_stats.csv")
+    if os.path.exists(stats):
+        for r in csv.DictReader(open(stats)):
+            k = _short(r["Name"])
+            if k:
+                out.append("| %s | %s | %.2f | %.2f | %.2f |" % (
+                    k, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                    float(r["MaxNs"]) / 1e3))
+    kib = {}
+    for counter in ("fetch", "write"):
+        path = os.path.join(d, counter, "run_counter_collection.csv")
+        if not os.path.exists(path):
+            continue
+        per = {}
+        for r in csv.DictReader(open(path)):
+            k = _short(r["Kernel_Name"])
+            if k:
+                per.setdefault(k, []).append(float(r["Counter_Value"]))
+        kib[counter] = {k: sum(v) / len(v) for k, v in per.items()}
+    traffic = None
+    if "fetch" in kib and "write" in kib and "copy" in kib["fetch"]:
+        ff = COPY_BYTES / 1024.0 / kib["fetch"]["copy"]
+        wf = COPY_BYTES / 1024.0 / kib["write"]["copy"]
+        out += ["", "FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f (the copy kernel moves %d B each way)"
+                % (ff, wf, COPY_BYTES), "",
+                "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per launch |",
+                "|---|---|---|---|"]
+        traffic = {"source_hash": kernel_source_hash(), "fetch_scale": ff, "write_scale": wf,
+                   "kernels": {}}
+        for k in sorted(kib["fetch"]):
+            if k == "copy" or k not in kib["write"]:
+                continue
+            b = kib["fetch"][k] * 1024 * ff + kib["write"][k] * 1024 * wf
+            traffic["kernels"][k] = {"fetch_kib": kib["fetch"][k], "write_kib": kib["write"][k],
+                                     "bytes_per_launch": round(b)}
+            out.append("| %s | %.1f | %.1f | %d |" % (k, kib["fetch"][k], kib["write"][k], b))
+        with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
+            json.dump(traffic, f, indent=1)
+    print("\n".join(out))
+
+
+def counter_run(torch, mgs, wl, dev, reps):
+    """Launches each hot kernel `reps` times with nothing else on the GPU but
+    the cache-evicting read between launches, so a counter collector sees
+    one dispatch per launch: the 256 MiB copy kernel (known traffic,
+    268435456 B read + written), dim0 on T (16640, 8192) G=64, dim1 on T^T
+    G=64, the MX cast on (131072, 5120) FLOOR and RCEIL."""
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    T = wl.token_major_gradient()
+    off = torch.from_numpy(wl.target_offsets(64)).to(dev)
+    x0 = torch.from_numpy(T.view(np.int16)).to(dev)
+    x1 = torch.from_numpy(np.ascontiguousarray(T.T).view(np.int16)).to(dev)
+    del T
+    c5 = wl.c5_mx()
+    x5 = torch.from_numpy(c5.x.view(np.int16)).to(dev)
+    del c5
+    q0, s0 = mgs.mgs_quant_groups_dim0(x0, off)
+    q1, s1 = mgs.mgs_quant_groups_dim1(x1, off)
+    q5, s5 = mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR)
+    runs = [lambda: mgs.mgs_copy(src, dst),
+            lambda: mgs.mgs_quant_groups_dim0(x0, off, q=q0, scales=s0),
+            lambda: mgs.mgs_quant_groups_dim1(x1, off, q=q1, scales=s1),
+            lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR, q=q5, scales=s5),
+            lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q5, scales=s5)]
+    for fn in runs:
+        for _ in range(reps):
+            flush.max()
+            fn()
+            torch.cuda.synchronize()
+    log("counter run done: %d launches of each kernel" % reps)
 
 
 def timed_us(torch, fn, flush, reps=20):
