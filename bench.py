@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("mgs_device.hpp", "mgs_kernels.hpp", "mgs_dim0.hip", "mgs_dim1.hip",
+KERNEL_SOURCES = ("mgs_device.hpp", "mgs_kernels.hpp", "mgs_dim0_layout.hpp", "mgs_dim0.hip", "mgs_dim1.hip",
                   "mgs_mx.hip", "mgs_api.hip")
 
 
@@ -51,7 +51,7 @@ def kernel_source_hash():
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if
     they were taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, "traffic.json")
+    path = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -167,9 +167,8 @@ def main():
     log("step: %.1f us; with events: dim0 %.1f us, dim1 %.1f us; %.0f GB/s"
         % (ms_per_step * 1e3, avg0 * 1e3, avg1 * 1e3, value))
 
-    # the dim0 entry point launches dim0_main_kernel, preceded by
-    # dim0_huge_partials_kernel when M > 5120; its event time covers both
-    dominant = "dim0_main_kernel" if avg0 >= avg1 else "dim1_kernel"
+    # each entry point launches one kernel here (dim0_kernel, dim1_kernel)
+    dominant = "dim0_kernel" if avg0 >= avg1 else "dim1_kernel"
     dom_ms, dom_bytes = (avg0, bytes_dim0) if avg0 >= avg1 else (avg1, bytes_dim1)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -223,8 +222,8 @@ def main():
 
 
 # kernel-name fragments of the library's kernels, and what each one is
-KERNELS = (("copy_kernel", "copy"), ("dim0_main_kernel", "dim0_main_kernel"),
-           ("dim0_huge_partials_kernel", "dim0_huge_partials_kernel"),
+KERNELS = (("copy_kernel", "copy"), ("dim0_kernel", "dim0_kernel"),
+           ("dim0_epoch_bump_kernel", "dim0_epoch_bump_kernel"),
            ("dim1_kernel", "dim1_kernel"), ("mx_kernel", "mx_kernel"))
 COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
 
@@ -329,6 +328,20 @@ def timed_us(torch, fn, flush, reps=20):
     return float(np.median(ts)), float(np.min(ts))
 
 
+def steady_us(torch, fn, reps=20):
+    """Average of `reps` back-to-back launches with no flush between them:
+    each launch also pays for writing back what the one before left dirty."""
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(reps):
+        fn()
+    b.record(st)
+    b.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
 def per_config_table(torch, mgs, wl, dev, T, Tt):
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
     rows = []
@@ -338,10 +351,14 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
         fn()
         torch.cuda.synchronize()
         med, mn = timed_us(torch, fn, flush)
+        sty = steady_us(torch, fn)
         rows.append({"config": name, "kind": kind, "us_median": round(med, 2), "us_min": round(mn, 2),
                      "algorithmic_GBps": round(bytes_ / (med * 1e-6) / 1e9, 1),
-                     "pct_hbm_peak": round(100 * bytes_ / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2)})
-        log("  %-44s %9.2f us  %7.1f GB/s" % (name, med, rows[-1]["algorithmic_GBps"]))
+                     "pct_hbm_peak": round(100 * bytes_ / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                     "us_steady": round(sty, 2),
+                     "steady_GBps": round(bytes_ / (sty * 1e-6) / 1e9, 1)})
+        log("  %-44s %9.2f us  %7.1f GB/s   back-to-back %9.2f us  %7.1f GB/s"
+            % (name, med, rows[-1]["algorithmic_GBps"], sty, rows[-1]["steady_GBps"]))
 
     def grouped(w):
         x = torch.from_numpy(w.x.view(np.int16)).to(dev)
@@ -350,9 +367,18 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
         q, s = f(x, o, w.pow2)
         return lambda: (lambda: f(x, o, w.pow2, q=q, scales=s))
 
-    log("per-config kernel times (cache flushed before each launch):")
-    for w in (wl.c1_dim0_small(), wl.c2_dim0_pow2(), wl.c3_dim0_large(),
-              wl.c6_dim0_target(64, T), wl.c4_dim1(1, T), wl.c4_dim1(16, T), wl.c4_dim1(64, T)):
+    log("per-config kernel times (cache flushed before each launch; then back-to-back launches):")
+    M = T.shape[0]
+    tall = [
+        # every row in one group: 26 chunks of 640 rows (column maxima through the workspace)
+        wl.Workload("dim0 (16640,8192) G=1", "dim0", T, np.array([M], dtype=np.int32)),
+        # eight groups of 2080 rows: 64-column strips, rows past 1280 read twice
+        wl.Workload("dim0 (16640,8192) G=8 even", "dim0", T,
+                    np.arange(1, 9, dtype=np.int32) * (M // 8)),
+    ]
+    for w in [wl.c1_dim0_small(), wl.c2_dim0_pow2(), wl.c3_dim0_large(),
+              wl.c6_dim0_target(64, T)] + tall + [wl.c4_dim1(1, T), wl.c4_dim1(16, T),
+                                                  wl.c4_dim1(64, T)]:
         add(w.name, w.kind, w.x, w.offsets, w.algorithmic_bytes(), grouped(w))
         del w
     c5 = wl.c5_mx()

@@ -2,6 +2,7 @@
 // argument checks, the dim0 workspace, and stream-ordered launches.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <map>
 #include <mutex>
@@ -22,24 +23,34 @@ int hip_status(hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Device workspace for the tall-group column partials of dim0, one buffer
-// per (device, stream) so concurrent streams never share it. Buffers grow on
-// demand and live until process exit.
+// Device workspace of dim0 for groups taller than 5120 rows (layout in
+// Dim0Workspace), one per (device, stream) so that concurrent streams never
+// share it. It grows on demand and lives until process exit. gen is the last
+// generation number handed to a kernel on that stream (1 .. 2^31 - 1).
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    uint32_t gen = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace>* g_ws = nullptr;
 
-hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
+// Returns the workspace of the current device and `stream` with at least
+// `bytes` bytes and the generation number of this call (0 when the stream is
+// capturing a graph: then the kernel reads it from the epoch word).
+// A new or regrown buffer is zeroed in stream order, and so is the whole
+// buffer whenever the host counter wraps.
+hipError_t dim0_workspace_for(hipStream_t stream, const mgs::Dim0Workspace& layout, bool capturing,
+                              void** out, uint32_t* gen) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
-    if (w.bytes < bytes) {
+    if (w.bytes < layout.bytes) {
+        // no allocation while a graph is being captured
+        if (capturing) return hipErrorStreamCaptureUnsupported;
         if (w.ptr) {
             // earlier work on this stream may still read the old buffer
             e = hipStreamSynchronize(stream);
@@ -49,14 +60,29 @@ hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
             w.ptr = nullptr;
             w.bytes = 0;
         }
-        e = hipMalloc(&w.ptr, bytes);
+        e = hipMalloc(&w.ptr, layout.bytes);
         if (e != hipSuccess) {
             w.ptr = nullptr;
             return e;
         }
-        w.bytes = bytes;
+        e = hipMemsetAsync(w.ptr, 0, layout.bytes, stream);
+        if (e != hipSuccess) return e;
+        w.bytes = layout.bytes;
+        w.gen = 0;
     }
     *out = w.ptr;
+    if (capturing) {
+        *gen = 0;
+        return hipSuccess;
+    }
+    if (w.gen >= 0x7FFFFFFFu) {
+        // wrapped: clear the workspace so that no stale word can hold the
+        // next generation
+        e = hipMemsetAsync(w.ptr, 0, w.bytes, stream);
+        if (e != hipSuccess) return e;
+        w.gen = 0;
+    }
+    *gen = ++w.gen;
     return hipSuccess;
 }
 
@@ -79,20 +105,25 @@ int check_grouped(const void* x, int64_t M, int64_t K, const int32_t* offsets, i
 
 namespace mgs {
 
-// Two 512-thread dim0 workgroups fit on a CU (104 VGPRs, 32 KiB of LDS each).
-int dim0_grid() {
+// Bound on a dim0 casting tile's wait for the column maxima of its group:
+// 20 ms of the device wall clock. MGS_DIM0_SPIN_TICKS overrides it (a
+// negative value skips the wait, which exercises the path that computes the
+// maxima in the casting tile itself).
+long long dim0_spin_ticks() {
+    if (const char* v = getenv("MGS_DIM0_SPIN_TICKS")) return atoll(v);
     static std::mutex mu;
-    static std::map<int, int> per_device;
+    static std::map<int, long long> per_device;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 512;
+    if (hipGetDevice(&dev) != hipSuccess) return 2000000;
     std::lock_guard<std::mutex> lock(mu);
     auto it = per_device.find(dev);
     if (it != per_device.end()) return it->second;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    per_device[dev] = 2 * cus;
-    return 2 * cus;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        khz = 100000;
+    const long long ticks = 20LL * khz;
+    per_device[dev] = ticks;
+    return ticks;
 }
 
 }  // namespace mgs
@@ -107,17 +138,28 @@ int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* of
     if (K % 8 != 0) return MGS_ERR_INVALID_ARG;
     if (K == 0) return MGS_OK;
     if (!scales || !aligned(scales, 16)) return MGS_ERR_INVALID_ARG;
+    if (mgs::dim0_tile_bound(M, K, n_groups) >= INT32_MAX) return MGS_ERR_UNSUPPORTED;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int64_t chunks = mgs::dim0_huge_chunk_bound(M);
+    const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);
     void* ws = nullptr;
-    if (chunks > 0) {
-        hipError_t e = workspace(s, (size_t)chunks * (size_t)K * sizeof(uint32_t), &ws);
+    uint32_t gen = 0;
+    if (layout.chunks > 0) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(s, &cap);
         if (e != hipSuccess) return hip_status(e);
+        const bool capturing = cap != hipStreamCaptureStatusNone;
+        e = dim0_workspace_for(s, layout, capturing, &ws, &gen);
+        if (e == hipErrorStreamCaptureUnsupported) return MGS_ERR_UNSUPPORTED;
+        if (e != hipSuccess) return hip_status(e);
+        if (capturing) {
+            e = mgs::launch_dim0_epoch_bump(ws, s);
+            if (e != hipSuccess) return hip_status(e);
+        }
     }
     return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, (int)K, offsets,
                                        n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
-                                       static_cast<uint8_t*>(q), scales,
-                                       static_cast<uint32_t*>(ws), mgs::dim0_grid(), s));
+                                       static_cast<uint8_t*>(q), scales, ws, gen,
+                                       mgs::dim0_spin_ticks(), s));
 }
 
 int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* offsets,

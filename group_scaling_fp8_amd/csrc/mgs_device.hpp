@@ -44,6 +44,26 @@ __device__ __forceinline__ uint32_t mag_fold(uint32_t w) {
     return max(w & 0xFFFFu, w >> 16);
 }
 
+// ---- streaming global accesses ----------------------------------------------
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 16 bytes of input read once: a nontemporal load, so the streamed input does
+// not push reusable lines out of L2 and the Infinity Cache.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// 8 bytes of output written once, with a nontemporal store.
+__device__ __forceinline__ void store_stream(void* p, uint2 v) {
+    u32x2 t;
+    t.x = v.x;
+    t.y = v.y;
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+}
+
 // ---- per-group scale ---------------------------------------------------------
 
 // amax15 is the bf16 magnitude pattern of the group's max |x|.

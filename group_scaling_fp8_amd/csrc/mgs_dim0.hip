@@ -8,27 +8,39 @@
 // size whatever the group sizes, so the grid scales with M * K and not with
 // the group count.
 //
-// Tiling (all decided on the device from the offsets; the host never reads
-// them). A workgroup has 512 threads and holds up to kSlabs 16-byte vectors
-// per thread in registers (160 KiB of bf16). Its tile is R rows of one group
-// times a strip of 8 * tpr columns, with tpr lanes per row:
-//   * class A, R <= 1280 rows: one pass. tpr is the widest power of two in
-//     [16, 128] whose tile still fits (short groups get strips up to 1024
-//     columns wide), or 8 (64-column strips) for groups of 641..1280 rows.
-//     Load -> column amax -> scale -> cast from registers -> store.
+// One launch, one tile per workgroup. The host sizes the grid with an upper
+// bound from (M, K, G) (it never reads the offsets); workgroups past the real
+// tile count exit as soon as they find no tile. Every wave finds its tile by
+// itself from the offsets (one vector load per 64 groups, DPP scans and a
+// ballot), so nothing stands between the launch and the tile's loads.
+// Offsets are sanitised on the fly: end[g] = min(max(off[0..g]), M), clamped
+// below at 0, so any offsets array gives in-range rows.
+//
+// A 512-thread workgroup holds up to kSlabs 16-byte vectors per thread in
+// registers (160 KiB of bf16). Its tile is R rows of one group times a strip
+// of 8 * tpr columns, with tpr lanes per row:
+//   * class A, R <= 1280: one pass. tpr is the widest power of two in
+//     [16, 128] whose tile fits (short groups get strips up to 1024 columns),
+//     or 8 (64-column strips) for 641..1280 rows. Load -> column amax ->
+//     scale -> cast from registers -> store.
 //   * class B, 1280 < R <= 5120: 64-column strips; the first 1280 rows stay in
-//     registers and the rest is read twice (once for the amax, once for the
-//     cast).
-//   * class C, R > 5120: the group is cut into chunks of at most 640 rows
-//     (128-column strips). A first kernel writes every chunk's column amax
-//     to a workspace; the main kernel combines them, then casts its chunk
-//     from registers. The chunk is read twice. That kernel is launched only
-//     when M > 5120.
-// Items are numbered group by group (chunk by chunk, strips fastest inside a
-// group) and the workgroups are persistent: workgroup b takes items b,
-// b + grid, ..., so workgroups that run at the same time read neighbouring
-// strips of the same rows. Every workgroup builds the group plan once, in
-// LDS, so an item costs no global lookup.
+//     registers and the rest is read twice (amax, then cast).
+//   * class C, R > 5120: chunks of at most 640 rows and 128-column strips,
+//     two tiles per (chunk, strip). Column-maximum tiles come first in the
+//     grid: each writes its chunk's column maxima to a workspace as 64-bit
+//     words, every word holding the call's generation number next to the
+//     maxima of two columns, each word one relaxed device-scope atomic store.
+//     The casting tiles come after every other tile's start; each reads the
+//     words of its strip with relaxed device-scope atomic loads until all of
+//     them carry this call's generation, combines the maxima and casts its
+//     chunk from registers (a chunk is read twice). A word is read and written
+//     whole, so the current generation implies the current maxima: no fence
+//     or flag is needed. The wait is bounded: past it the tile computes the
+//     column amax of the whole group itself, so the result never depends on
+//     the order in which workgroups run.
+// Tile order: all column-maximum tiles (group by group), then every group's
+// own tiles (class C: its casting tiles), chunk by chunk with strips fastest,
+// so workgroups that run together read neighbouring strips of the same rows.
 #include "mgs_device.hpp"
 #include "mgs_kernels.hpp"
 
@@ -42,123 +54,169 @@ constexpr int kCap = kThreads * kSlabs;               // vectors per tile
 constexpr int kRowsW64 = kCap / 8;                    // 1280 rows at 64 columns
 constexpr int kRowsW128 = kCap / 16;                  // 640 rows at 128 columns
 static_assert(kRowsW128 == kDim0HugeChunkRows, "chunk size mismatch");
-static_assert(kRowsW64 * 4 == kDim0HugeRows, "huge-group threshold mismatch");
+static_assert(kRowsW64 * 4 == kDim0HugeRows, "tall-group threshold mismatch");
+static_assert((kCap >> 7) == 80 && (kCap >> 6) == 160 && (kCap >> 5) == 320,
+              "strip steps assumed by dim0_tile_bound");
+constexpr int kStreamSlabs = 4;                       // rows in flight per lane for streamed rows
 
 enum { kClassA = 0, kClassB = 1, kClassC = 2 };
 
 struct Tile {
-    int g;          // group, or -1 when the item does not exist
+    int g;          // group, or -1 when this workgroup has no tile
+    int maxima;     // 1: class C column-maximum tile (writes no output)
     int cls;        // kClassA / kClassB / kClassC
     int lt;         // log2 of lanes per row (3..7)
     int strip;      // column strip index (strip width 8 << lt)
     int c, nc;      // chunk index and chunk count (class C), else 0 and 1
     int r0, r1;     // rows of this tile (the chunk for class C)
-    int cbase;      // class C: index of the group's first chunk in the workspace
+    int g0, g1;     // rows of the whole group
+    int cbase;      // class C: workspace row of the group's first chunk
 };
 
-// Log2 lanes per row for a group of R rows, and its class.
-__device__ __forceinline__ void choose_tiling(int R, int K, int* lt_out, int* cls_out) {
-    int lt, cls;
+// Per-lane view of one group: rows, class, strips, chunks and tile counts.
+struct GroupInfo {
+    int start, R, lt, cls, ns, nc;
+    int cnt_x;      // column-maximum tiles
+    int cnt_m;      // own tiles (class C: casting tiles)
+    int chunks;     // class C chunks
+};
+
+__device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, int K) {
+    GroupInfo gi;
+    gi.start = start;
+    gi.R = end - start;
+    const int R = gi.R;
     if (R > kDim0HugeRows) {
-        lt = 4;
-        cls = kClassC;
+        gi.lt = 4;
+        gi.cls = kClassC;
     } else if (R > kRowsW64) {
-        lt = 3;
-        cls = kClassB;
+        gi.lt = 3;
+        gi.cls = kClassB;
     } else if (R > kRowsW128) {
-        lt = 3;
-        cls = kClassA;
+        gi.lt = 3;
+        gi.cls = kClassA;
     } else {
-        lt = 7;
-        while (lt > 4 && R * (1 << lt) > kCap) --lt;
-        cls = kClassA;
+        gi.lt = R <= (kCap >> 7) ? 7 : (R <= (kCap >> 6) ? 6 : (R <= (kCap >> 5) ? 5 : 4));
+        gi.cls = kClassA;
     }
     // no strip wider than needed to cover K
-    while (lt > 3 && (8 << (lt - 1)) >= K) --lt;
-    *lt_out = lt;
-    *cls_out = cls;
+    while (gi.lt > 3 && (8 << (gi.lt - 1)) >= K) --gi.lt;
+    gi.ns = (K + (8 << gi.lt) - 1) >> (gi.lt + 3);
+    gi.nc = gi.cls == kClassC ? (R + kRowsW128 - 1) / kRowsW128 : 1;
+    gi.chunks = (valid && gi.cls == kClassC) ? gi.nc : 0;
+    gi.cnt_x = gi.chunks * gi.ns;
+    gi.cnt_m = valid ? gi.nc * gi.ns : 0;
+    return gi;
 }
 
-// Per-workgroup plan of every group, in LDS: first row, rows, class, log2
-// lanes per row, strip count, chunk count, end of its item range and (class C)
-// index of its first chunk in the workspace. Built once per workgroup by
-// wave 0. Offsets are sanitised on the fly: end[g] = min(max(off[0..g]), M),
-// clamped below at 0, so any offsets array gives in-range rows.
-struct Plan {
-    int start[kMaxGroups];
-    int rows[kMaxGroups];
-    int code[kMaxGroups];     // cls | lt << 4
-    int iend[kMaxGroups];     // inclusive prefix of items, in group order
-    int cbase[kMaxGroups];    // class C: first workspace chunk of the group
-    int total;
-};
+// Inclusive prefix sum over a wave with DPP: row shifts 1, 2, 4, 8 inside
+// each 16-lane row, then the row_bcast:15 / row_bcast:31 carries.
+__device__ __forceinline__ int wave_prefix_sum_dpp(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+    return v;
+}
 
-// huge_only: count only the class C chunks (the partial-amax kernel's items)
-__device__ void build_plan(const int32_t* __restrict__ off, int G, int M, int K, bool huge_only,
-                           Plan* p) {
-    if (threadIdx.x >= kWave) return;
-    const int lane = threadIdx.x;
-    int carry_end = 0, carry_cnt = 0, carry_chunks = 0;
+// Fills t from lane src's group, tile `local` inside that group. src is
+// wave-uniform, so the fields land in scalar registers.
+__device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chunk_incl, int src,
+                                          int g, int local, int maxima) {
+    const int ns = __builtin_amdgcn_readlane(gi.ns, src);
+    const int nc = __builtin_amdgcn_readlane(gi.nc, src);
+    const int start = __builtin_amdgcn_readlane(gi.start, src);
+    const int R = __builtin_amdgcn_readlane(gi.R, src);
+    t.g = g;
+    t.maxima = maxima;
+    t.cls = __builtin_amdgcn_readlane(gi.cls, src);
+    t.lt = __builtin_amdgcn_readlane(gi.lt, src);
+    t.nc = nc;
+    t.c = nc > 1 ? local / ns : 0;
+    t.strip = local - t.c * ns;
+    t.g0 = start;
+    t.g1 = start + R;
+    if (t.cls == kClassC) {
+        const int cs = (R + nc - 1) / nc;
+        t.r0 = min(start + t.c * cs, t.g1);
+        t.r1 = min(start + (t.c + 1) * cs, t.g1);
+    } else {
+        t.r0 = t.g0;
+        t.r1 = t.g1;
+    }
+    t.cbase = __builtin_amdgcn_readlane(chunk_incl, src) - __builtin_amdgcn_readlane(gi.chunks, src);
+}
+
+// Tile number `target` of the order described at the top of this file. Run
+// by every wave of the workgroup; all lanes return the same tile.
+__device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int target) {
+    const int lane = threadIdx.x & (kWave - 1);
+    Tile t;
+    t.g = -1;
+    // One pass finds a column-maximum tile, or an own tile provided there are
+    // no column-maximum tiles at all (their count is known only at the end).
+    int carry_end = 0, carry_x = 0, carry_m = 0, carry_ch = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
-        int raw = g < G ? off[g] : M;
-        raw = min(max(raw, 0), M);
-        const int end = max(wave_prefix_imax(raw), carry_end);
+        const int raw = min(max(g < G ? off[g] : M, 0), M);
+        const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         int start = __shfl_up(end, 1, kWave);
         if (lane == 0) start = carry_end;
-        const int R = end - start;
-        int lt, cls;
-        choose_tiling(R, K, &lt, &cls);
-        const int ns = (K + (8 << lt) - 1) / (8 << lt);
-        const int nc = cls == kClassC ? (R + kRowsW128 - 1) / kRowsW128 : 1;
-        const int chunks_c = (g < G && cls == kClassC) ? nc : 0;
-        int cnt = 0;
-        if (g < G) cnt = huge_only ? chunks_c * ns : nc * ns;
-        const int incl = wave_prefix_sum(cnt) + carry_cnt;
-        const int cincl = wave_prefix_sum(chunks_c) + carry_chunks;
-        if (g < G) {
-            p->start[g] = start;
-            p->rows[g] = R;
-            p->code[g] = cls | (lt << 4);
-            p->iend[g] = incl;
-            p->cbase[g] = cincl - chunks_c;
+        const GroupInfo gi = group_info(start, end, g < G, K);
+        const int incl_x = wave_prefix_sum_dpp(gi.cnt_x) + carry_x;
+        const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
+        const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
+        const uint64_t hx = __ballot(gi.cnt_x > 0 && target >= incl_x - gi.cnt_x && target < incl_x);
+        if (hx) {
+            const int src = __ffsll((unsigned long long)hx) - 1;
+            const int local = target - (__builtin_amdgcn_readlane(incl_x, src) -
+                                        __builtin_amdgcn_readlane(gi.cnt_x, src));
+            take_tile(t, gi, incl_ch, src, base + src, local, 1);
+            return t;
         }
-        carry_end = __shfl(end, kWave - 1, kWave);
-        carry_cnt = __shfl(incl, kWave - 1, kWave);
-        carry_chunks = __shfl(cincl, kWave - 1, kWave);
+        if (t.g < 0) {
+            const uint64_t hm = __ballot(gi.cnt_m > 0 && target >= incl_m - gi.cnt_m && target < incl_m);
+            if (hm) {
+                const int src = __ffsll((unsigned long long)hm) - 1;
+                const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
+                                            __builtin_amdgcn_readlane(gi.cnt_m, src));
+                take_tile(t, gi, incl_ch, src, base + src, local, 0);
+            }
+        }
+        carry_end = __builtin_amdgcn_readlane(end, kWave - 1);
+        carry_x = __builtin_amdgcn_readlane(incl_x, kWave - 1);
+        carry_m = __builtin_amdgcn_readlane(incl_m, kWave - 1);
+        carry_ch = __builtin_amdgcn_readlane(incl_ch, kWave - 1);
     }
-    if (lane == 0) p->total = carry_cnt;
-}
-
-// Tile of item `item` (item < p->total): the group is the first g with
-// iend[g] > item; inside a group items run chunk by chunk, strips fastest.
-__device__ __forceinline__ Tile tile_of(const Plan* p, int G, int K, int item) {
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (p->iend[mid] > item) hi = mid; else lo = mid + 1;
+    if (carry_x == 0) return t;
+    // There are column-maximum tiles, and target lies past them: search the
+    // own tiles again with their count taken off.
+    target -= carry_x;
+    t.g = -1;
+    carry_end = carry_m = carry_ch = 0;
+    for (int base = 0; base < G; base += kWave) {
+        const int g = base + lane;
+        const int raw = min(max(g < G ? off[g] : M, 0), M);
+        const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
+        int start = __shfl_up(end, 1, kWave);
+        if (lane == 0) start = carry_end;
+        const GroupInfo gi = group_info(start, end, g < G, K);
+        const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
+        const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
+        const uint64_t hm = __ballot(gi.cnt_m > 0 && target >= incl_m - gi.cnt_m && target < incl_m);
+        if (hm) {
+            const int src = __ffsll((unsigned long long)hm) - 1;
+            const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
+                                        __builtin_amdgcn_readlane(gi.cnt_m, src));
+            take_tile(t, gi, incl_ch, src, base + src, local, 0);
+            return t;
+        }
+        carry_end = __builtin_amdgcn_readlane(end, kWave - 1);
+        carry_m = __builtin_amdgcn_readlane(incl_m, kWave - 1);
+        carry_ch = __builtin_amdgcn_readlane(incl_ch, kWave - 1);
     }
-    Tile t;
-    const int g = lo;
-    const int code = p->code[g];
-    t.g = g;
-    t.cls = code & 15;
-    t.lt = code >> 4;
-    const int ns = (K + (8 << t.lt) - 1) / (8 << t.lt);
-    const int R = p->rows[g], start = p->start[g];
-    t.nc = t.cls == kClassC ? (R + kRowsW128 - 1) / kRowsW128 : 1;
-    const int local = item - (p->iend[g] - t.nc * ns);
-    t.c = local / ns;
-    t.strip = local - t.c * ns;
-    if (t.cls == kClassC) {
-        const int cs = (R + t.nc - 1) / t.nc;
-        t.r0 = min(start + t.c * cs, start + R);
-        t.r1 = min(start + (t.c + 1) * cs, start + R);
-    } else {
-        t.r0 = start;
-        t.r1 = start + R;
-    }
-    t.cbase = p->cbase[g];
     return t;
 }
 
@@ -204,7 +262,7 @@ __device__ __forceinline__ TileGeom tile_geom(const Tile& t, int K) {
     return q;
 }
 
-// Loads the first nreg rows of the tile into registers (zeros elsewhere).
+// Loads rows [r0, r0 + nreg) of this lane's 8 columns into registers.
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t K, int r0, int nreg,
                                           const TileGeom& q, uint4 (&v)[kSlabs]) {
 #pragma unroll
@@ -213,91 +271,119 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
         if (s * q.rps < nreg) {
             const int rr = s * q.rps + q.ty;
             if (rr < nreg && q.col_ok)
-                v[s] = *reinterpret_cast<const uint4*>(x + (int64_t)(r0 + rr) * K + q.col);
+                v[s] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
         }
     }
 }
 
-constexpr int kStreamSlabs = 4;     // rows in flight per lane for streamed (class B) rows
+// Running column amax of rows [r0 + from, r0 + to) of this lane's columns,
+// streamed through a few registers.
+__device__ __forceinline__ void stream_amax(const uint16_t* __restrict__ x, int64_t K, int r0, int from,
+                                            int to, const TileGeom& q, uint4& m) {
+    for (int base = from; base < to; base += kStreamSlabs * q.rps) {
+        uint4 u[kStreamSlabs];
+#pragma unroll
+        for (int b = 0; b < kStreamSlabs; ++b) {
+            u[b] = make_uint4(0u, 0u, 0u, 0u);
+            const int rr = base + b * q.rps + q.ty;
+            if (rr < to && q.col_ok)
+                u[b] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
+        }
+#pragma unroll
+        for (int b = 0; b < kStreamSlabs; ++b) max4(m, u[b]);
+    }
+}
+
+__device__ __forceinline__ uint64_t load_agent(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace
 
-// Class C first pass: column amax of every (chunk, 128-column strip) of the
-// groups taller than kDim0HugeRows, to ws[chunk * K + column]. Persistent:
-// workgroup b takes items b, b + grid, ...; it exits at once when no group
-// is that tall.
-__global__ __launch_bounds__(kThreads) void dim0_huge_partials_kernel(
+// ws layout (Dim0Workspace): the epoch word, then maxima[chunk][K / 2]
+// 64-bit words (generation << 32 | two 16-bit magnitude patterns).
+__global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
-        uint32_t* __restrict__ ws) {
-    __shared__ Plan plan;
-    __shared__ uint4 red[kThreads];
-    build_plan(off, G, M, K, true, &plan);
-    __syncthreads();
-    for (int item = blockIdx.x; item < plan.total; item += gridDim.x) {
-        const Tile t = tile_of(&plan, G, K, item);
-        const TileGeom q = tile_geom(t, K);
-        const int nrows = t.r1 - t.r0;
-        uint4 v[kSlabs];
-        load_tile(x, K, t.r0, nrows, q, v);
-        uint4 m = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int s = 0; s < kSlabs; ++s)
-            if (s * q.rps < nrows) max4(m, v[s]);
-        m = block_column_amax(m, q.tpr, red);
-        if (threadIdx.x < q.tpr && q.col_ok) {
-            uint32_t* dst = ws + (int64_t)(t.cbase + t.c) * K + q.col;
-            reinterpret_cast<uint4*>(dst)[0] = make_uint4(m.x & 0xFFFFu, m.x >> 16, m.y & 0xFFFFu, m.y >> 16);
-            reinterpret_cast<uint4*>(dst)[1] = make_uint4(m.z & 0xFFFFu, m.z >> 16, m.w & 0xFFFFu, m.w >> 16);
-        }
-        __syncthreads();     // red is reused by the next item
-    }
-}
-
-// Main pass, persistent: workgroup b takes items b, b + grid, ... of every
-// group, empty groups included (they write their scale row).
-__global__ __launch_bounds__(kThreads) void dim0_main_kernel(
-        const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
-        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales,
-        const uint32_t* __restrict__ ws) {
-    __shared__ Plan plan;
+        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles,
+        const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max, uint32_t gen_arg,
+        long long spin_ticks) {
     __shared__ uint4 red[kThreads];
     __shared__ float s_scale[128 * 8];
-    build_plan(off, G, M, K, false, &plan);
-    __syncthreads();
-    const bool p2 = pow2 != 0;
-    for (int item = blockIdx.x; item < plan.total; item += gridDim.x) {
-        const Tile t = tile_of(&plan, G, K, item);
+
+    // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
+    for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
+        const Tile t = find_tile(off, G, M, K, (int)item);
+        if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);
         const int nrows = t.r1 - t.r0;
         const int nreg = min(nrows, geo.rps * kSlabs);     // rows held in registers
 
+        uint4 m = make_uint4(0u, 0u, 0u, 0u);
+        if (!t.maxima && t.cls == kClassC) {
+            // casting tile of a tall group: wait, bounded, until the maxima of
+            // every chunk of this strip carry this call's generation; before
+            // the tile's own loads, so that no tile data sits in registers
+            // meanwhile. Lane (tx, ty) reads chunks ty, ty + rps, ...
+            const uint32_t gen = gen_arg ? gen_arg : *ws_epoch;
+            bool ok = spin_ticks >= 0;
+            if (ok && geo.col_ok) {
+                const long long t0 = wall_clock64();
+                for (int c = geo.ty; c < t.nc && ok; c += geo.rps) {
+                    const uint64_t* src = ws_max + (((int64_t)(t.cbase + c) * K + geo.col) >> 1);
+                    uint64_t w0, w1, w2, w3;
+                    for (;;) {
+                        w0 = load_agent(src);
+                        w1 = load_agent(src + 1);
+                        w2 = load_agent(src + 2);
+                        w3 = load_agent(src + 3);
+                        if ((uint32_t)(w0 >> 32) == gen && (uint32_t)(w1 >> 32) == gen &&
+                            (uint32_t)(w2 >> 32) == gen && (uint32_t)(w3 >> 32) == gen)
+                            break;
+                        if (wall_clock64() - t0 > spin_ticks) {
+                            ok = false;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(8);
+                    }
+                    if (ok) max4(m, make_uint4((uint32_t)w0, (uint32_t)w1, (uint32_t)w2, (uint32_t)w3));
+                }
+            }
+            if (!__syncthreads_and(ok)) {
+                // some maxima did not come in time: the column amax of the whole group
+                m = make_uint4(0u, 0u, 0u, 0u);
+                stream_amax(x, K, t.g0, 0, t.g1 - t.g0, geo, m);
+            }
+        }
+
         uint4 v[kSlabs];
         load_tile(x, K, t.r0, nreg, geo, v);
 
-        uint4 m = make_uint4(0u, 0u, 0u, 0u);
-        if (t.cls == kClassC) {
-            // column amax of the whole group from the first pass's partials
-            if (geo.col_ok) {
-                for (int c = geo.ty; c < t.nc; c += geo.rps) {
-                    const uint4* src = reinterpret_cast<const uint4*>(ws + (int64_t)(t.cbase + c) * K + geo.col);
-                    const uint4 a = src[0], b = src[1];
-                    max4(m, make_uint4(a.x | (a.y << 16), a.z | (a.w << 16), b.x | (b.y << 16), b.z | (b.w << 16)));
-                }
+        if (t.maxima) {
+            // class C column-maximum tile: publish this chunk's column maxima
+            const uint32_t gen = gen_arg ? gen_arg : *ws_epoch;
+#pragma unroll
+            for (int s = 0; s < kSlabs; ++s)
+                if (s * geo.rps < nreg) max4(m, v[s]);
+            m = block_column_amax(m, geo.tpr, red);
+            if (threadIdx.x < geo.tpr && geo.col_ok) {
+                uint64_t* dst = ws_max + (((int64_t)(t.cbase + t.c) * K + geo.col) >> 1);
+                const uint64_t g = (uint64_t)gen << 32;
+                store_agent(dst, g | m.x);
+                store_agent(dst + 1, g | m.y);
+                store_agent(dst + 2, g | m.z);
+                store_agent(dst + 3, g | m.w);
             }
-        } else {
+            __syncthreads();
+            continue;     // the barrier above ends this item's reads of red
+        }
+
+        if (t.cls != kClassC) {
             // class B: rows past the register capacity are streamed for the amax
-            for (int base = nreg; base < nrows; base += kStreamSlabs * geo.rps) {
-                uint4 u[kStreamSlabs];
-#pragma unroll
-                for (int b = 0; b < kStreamSlabs; ++b) {
-                    u[b] = make_uint4(0u, 0u, 0u, 0u);
-                    const int rr = base + b * geo.rps + geo.ty;
-                    if (rr < nrows && geo.col_ok)
-                        u[b] = *reinterpret_cast<const uint4*>(x + (int64_t)(t.r0 + rr) * K + geo.col);
-                }
-#pragma unroll
-                for (int b = 0; b < kStreamSlabs; ++b) max4(m, u[b]);
-            }
+            stream_amax(x, K, t.r0, nreg, nrows, geo, m);
 #pragma unroll
             for (int s = 0; s < kSlabs; ++s)
                 if (s * geo.rps < nreg) max4(m, v[s]);
@@ -305,6 +391,7 @@ __global__ __launch_bounds__(kThreads) void dim0_main_kernel(
         m = block_column_amax(m, geo.tpr, red);
 
         if (threadIdx.x < geo.tpr) {
+            const bool p2 = pow2 != 0;
             float s[8];
             s[0] = group_scale(m.x & 0xFFFFu, p2);
             s[1] = group_scale(m.x >> 16, p2);
@@ -332,8 +419,8 @@ __global__ __launch_bounds__(kThreads) void dim0_main_kernel(
                 if (s * geo.rps < nreg) {
                     const int rr = s * geo.rps + geo.ty;
                     if (rr < nreg)
-                        *reinterpret_cast<uint2*>(q + (int64_t)(t.r0 + rr) * K + geo.col) =
-                            cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7);
+                        store_stream(q + (int64_t)(t.r0 + rr) * K + geo.col,
+                                     cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
                 }
             }
             // class B: second read of the streamed rows
@@ -343,31 +430,49 @@ __global__ __launch_bounds__(kThreads) void dim0_main_kernel(
                 for (int b = 0; b < kStreamSlabs; ++b) {
                     u[b] = make_uint4(0u, 0u, 0u, 0u);
                     const int rr = base + b * geo.rps + geo.ty;
-                    if (rr < nrows) u[b] = *reinterpret_cast<const uint4*>(x + (int64_t)(t.r0 + rr) * K + geo.col);
+                    if (rr < nrows) u[b] = load_stream(x + (int64_t)(t.r0 + rr) * K + geo.col);
                 }
 #pragma unroll
                 for (int b = 0; b < kStreamSlabs; ++b) {
                     const int rr = base + b * geo.rps + geo.ty;
                     if (rr < nrows)
-                        *reinterpret_cast<uint2*>(q + (int64_t)(t.r0 + rr) * K + geo.col) =
-                            cast8(u[b], s0, s1, s2, s3, s4, s5, s6, s7);
+                        store_stream(q + (int64_t)(t.r0 + rr) * K + geo.col,
+                                     cast8(u[b], s0, s1, s2, s3, s4, s5, s6, s7));
                 }
             }
         }
-        __syncthreads();     // s_scale and red are reused by the next item
+        __syncthreads();     // s_scale is reused by the next item
+    }
+}
+
+// Advances the epoch word by one, keeping its top bit set so that epochs
+// never equal a host-chosen generation (top bit clear).
+__global__ void dim0_epoch_bump_kernel(uint32_t* __restrict__ ws_epoch) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        uint32_t n = (*ws_epoch & 0x7FFFFFFFu) + 1u;
+        if (n > 0x7FFFFFFFu) n = 1u;
+        *ws_epoch = 0x80000000u | n;
     }
 }
 
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, bool pow2,
-                       uint8_t* q, float* scales, uint32_t* ws, int grid, hipStream_t stream) {
-    if (M > kDim0HugeRows) {
-        hipLaunchKernelGGL(dim0_huge_partials_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, x, M, K, off, G, ws);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(dim0_main_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, M, K,
-                       off, G, pow2 ? 1 : 0, q, scales, ws);
+                       uint8_t* q, float* scales, void* ws, uint32_t gen, long long spin_ticks,
+                       hipStream_t stream) {
+    const int64_t n_tiles = dim0_tile_bound(M, K, G);
+    if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
+    const int64_t grid = n_tiles < kDim0MaxGrid ? n_tiles : kDim0MaxGrid;
+    const Dim0Workspace w = dim0_workspace(M, K);
+    char* base = static_cast<char*>(ws);
+    const uint32_t* ws_epoch = base ? reinterpret_cast<const uint32_t*>(base + w.epoch_off) : nullptr;
+    uint64_t* ws_max = base ? reinterpret_cast<uint64_t*>(base + w.max_off) : nullptr;
+    hipLaunchKernelGGL(dim0_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, M, K, off,
+                       G, pow2 ? 1 : 0, q, scales, (int)n_tiles, ws_epoch, ws_max, gen, spin_ticks);
+    return hipGetLastError();
+}
+
+hipError_t launch_dim0_epoch_bump(void* ws, hipStream_t stream) {
+    hipLaunchKernelGGL(dim0_epoch_bump_kernel, dim3(1), dim3(64), 0, stream,
+                       reinterpret_cast<uint32_t*>(static_cast<char*>(ws)));
     return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const uint16_t* __restrict
     for (int j = 0; j < kMxVecs; ++j) {
         const int64_t vi = base + (int64_t)j * kThreads;
         v[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (vi < n_vec) v[j] = reinterpret_cast<const uint4*>(x)[vi];
+        if (vi < n_vec) v[j] = load_stream(reinterpret_cast<const uint4*>(x) + vi);
     }
 #pragma unroll
     for (int j = 0; j < kMxVecs; ++j) {
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const uint16_t* __restrict
         byte = max(byte, 0);
         const float mult = __uint_as_float((uint32_t)(254 - byte) << 23);
         if (vi < n_vec) {
-            reinterpret_cast<uint2*>(q)[vi] = cast8(v[j], mult);
+            store_stream(reinterpret_cast<uint2*>(q) + vi, cast8(v[j], mult));
             if ((lane & 3) == 0) scales[vi >> 2] = (uint8_t)byte;
         }
     }

@@ -73,11 +73,22 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * Requirements: M >= 0, K >= 0, K % 8 == 0; x 16-byte aligned, q 8-byte
  * aligned, scales 16-byte aligned. M == 0 writes only the scales; K == 0 is a
  * no-op.
- * Memory: when M > 5120, groups taller than 5120 rows are cut into chunks
- * whose column maxima go through a device workspace of about
- * (M / 568) * K * 4 bytes. The library allocates it once per (device, stream)
- * with hipMalloc, grows it as needed, and frees it only at process exit. A
- * call that has to grow it is not graph-capture safe.
+ * Memory: when M > 5120, a group taller than 5120 rows is cut into chunks of
+ * at most 640 rows. Each chunk's column maxima go through a device workspace
+ * of about (M / 568) * K * 4 bytes. Inside the one kernel launch the casting
+ * tiles wait for them, and the wait is bounded: past about 20 ms of device
+ * wall clock a tile computes them itself, so the result never depends on
+ * workgroup scheduling. The environment variable MGS_DIM0_SPIN_TICKS, read
+ * on every call, sets that bound in wall-clock ticks; a negative value skips
+ * the wait. The library allocates the workspace once per (device, stream)
+ * with hipMalloc, zeroes it, grows it as needed, and frees it only at process
+ * exit. Graph capture: a call on a capturing stream adds one single-thread
+ * kernel before the main one and replays correctly. When M > 5120 it needs
+ * the workspace to exist already, so make one call of at least that size
+ * eagerly on the same stream first. Otherwise it returns
+ * MGS_ERR_UNSUPPORTED. Replays use the capturing stream's workspace, so they
+ * must not overlap other calls made on that stream.
+ * Errors: MGS_ERR_UNSUPPORTED if the tile count bound reaches 2^31.
  */
 int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
                           const int32_t *offsets, int32_t n_groups,

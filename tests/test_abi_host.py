@@ -70,6 +70,8 @@ def test_grouped_argument_errors(L, fn):
     if fn.endswith("dim0"):
         assert call(K=12) == INVALID
         assert call(s=A + 4) == INVALID
+        # 1024 groups of 1024-column strips over K = 2^31 - 8: the tile bound reaches 2^31
+        assert call(K=(1 << 31) - 8, G=1024) == UNSUPPORTED
     else:
         assert call(K=24) == INVALID
         assert call(s=A + 2) == INVALID

@@ -1,0 +1,114 @@
+"""CPU check of the dim0 grid bound (mgs_dim0_layout.hpp).
+
+The dim0 launch has one workgroup per tile and sizes its grid from (M, K, G)
+alone, so the bound must hold for every way of splitting M rows into G
+groups. The tile count of a group depends only on its row count, as a step
+function, so the worst split is found exactly by a knapsack over the first
+row count of each step (0, 81, 161, 321, 641, then 640 * (c - 1) + 1 for the
+chunked groups). The C++ bound, compiled with g++ from the header the library
+uses, must be at least that worst case."""
+import math
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                    "group_scaling_fp8_amd", "csrc")
+
+DRIVER = r"""
+#include <stdio.h>
+#include "mgs_dim0_layout.hpp"
+int main() {
+    long long M, K, G;
+    while (scanf("%lld %lld %lld", &M, &K, &G) == 3)
+        printf("%lld %lld\n", (long long)mgs::dim0_tile_bound(M, K, G),
+               (long long)mgs::dim0_huge_chunk_bound(M));
+    return 0;
+}
+"""
+
+
+def tiles(R, K):
+    """Tiles of one group of R rows (the rule the kernel's tile search uses)."""
+    if R > 5120:
+        lt, chunked = 4, True
+    elif R > 640:
+        lt, chunked = 3, False
+    else:
+        lt = 7 if R <= 80 else 6 if R <= 160 else 5 if R <= 320 else 4
+        chunked = False
+    while lt > 3 and (8 << (lt - 1)) >= K:
+        lt -= 1
+    ns = -(-K // (8 << lt))
+    return 2 * ns * -(-R // 640) if chunked else ns
+
+
+def worst_splits(Mmax, K, Gmax):
+    """best[G][M] = the most tiles over all splits of at most M rows into
+    exactly G groups."""
+    sizes = [0, 81, 161, 321, 641] + [640 * (c - 1) + 1 for c in range(9, Mmax // 640 + 3)]
+    sizes = [r for r in sizes if r <= Mmax]
+    NEG = -(1 << 40)
+    dp = np.full(Mmax + 1, NEG, np.int64)
+    dp[0] = 0
+    best = [np.maximum.accumulate(dp)]
+    for _ in range(Gmax):
+        nxt = np.full(Mmax + 1, NEG, np.int64)
+        for r in sizes:
+            t = tiles(r, K)
+            np.maximum(nxt[r:], dp[:Mmax + 1 - r] + t, out=nxt[r:])
+        dp = nxt
+        best.append(np.maximum.accumulate(dp))
+    return best
+
+
+@pytest.fixture(scope="module")
+def bound_tool():
+    d = tempfile.mkdtemp(prefix="mgs_bound_")
+    src = os.path.join(d, "bound.cpp")
+    exe = os.path.join(d, "bound")
+    with open(src, "w") as f:
+        f.write(DRIVER)
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", CSRC, "-o", exe, src], check=True)
+
+    def run(triples):
+        inp = "".join("%d %d %d\n" % t for t in triples)
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+        return [tuple(int(v) for v in line.split()) for line in out.splitlines()]
+    return run
+
+
+@pytest.mark.parametrize("K", [8, 64, 72, 136, 1032, 8192])
+def test_bound_covers_the_worst_split(bound_tool, K):
+    Mmax, Gmax = 17000, 64
+    best = worst_splits(Mmax, K, Gmax)
+    Ms = [0, 1, 80, 81, 400, 641, 1300, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
+    Gs = [1, 2, 3, 7, 16, 64]
+    triples = [(M, K, G) for M in Ms for G in Gs]
+    got = bound_tool(triples)
+    for (M, _, G), (b, _) in zip(triples, got):
+        exact = int(best[G][M])
+        assert b >= exact, (M, K, G, b, exact)
+        # and it is no wild over-estimate (the grid's extra workgroups exit at once)
+        assert b <= 2 * exact + 16, (M, K, G, b, exact)
+
+
+def test_bound_of_the_benchmark_shape(bound_tool):
+    (b, chunks), = bound_tool([(16640, 8192, 64)])
+    exact = int(worst_splits(16640, 8192, 64)[64][16640])
+    assert exact <= b == 4229
+    assert chunks == 16640 // 640 + 16640 // 5121
+
+
+def test_chunk_bound_covers_every_chunked_split(bound_tool):
+    # the chunked groups of any split have at most dim0_huge_chunk_bound(M) chunks
+    for M in (5121, 5760, 5761, 10242, 10243, 16640, 40000):
+        (_, chunks), = bound_tool([(M, 8, 1)])
+        worst = 0
+        for n in range(1, M // 5121 + 1):           # n groups of just over 5120 rows
+            rows = M // n
+            worst = max(worst, n * math.ceil(rows / 640))
+        assert chunks >= worst, (M, chunks, worst)

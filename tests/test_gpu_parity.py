@@ -213,7 +213,7 @@ def edge_values(rng, shape):
     (1500, 128, [0, 1024, 3, 473]),              # tall group next to tiny ones
     (2000, 384, [700, 0, 0, 1300]),              # 64-column strips, and one group read twice
     (96, 64, [32, 32, 32]),
-    (12000, 136, [0, 11000, 1000]),              # a group cut into chunks (first pass + workspace)
+    (12000, 136, [0, 11000, 1000]),              # a group cut into chunks (maxima through the workspace)
     (7000, 512, [5121, 1279, 600]),              # just over the chunking threshold
     (6000, 64, [5120, 880]),                     # just under it, with 64-column rows
 ])
