@@ -62,6 +62,42 @@ def measured_traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
+class HipEvent:
+    """A HIP event created with hipEventDisableSystemFence: it records a
+    timestamp on the stream without the system-scope cache writeback and
+    invalidate of a default event, which would otherwise add several
+    microseconds between the kernels it separates. Elapsed times are read
+    only after a device synchronisation."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            # the HIP runtime torch has loaded (one copy per process, by soname)
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._c = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(0x20000000))
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+
+    def record(self, stream):
+        rc = HipEvent._hip.hipEventRecord(self.ev, self._c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_ms(self, end):
+        ms = self._c.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -130,15 +166,9 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         mgs.mgs_quant_groups_dim0(x0, o, False, q=q0, scales=s0)
-        if ev is not None:
-            ev[1].record(stream)
         mgs.mgs_quant_groups_dim1(x1, o, False, q=q1, scales=s1)
-        if ev is not None:
-            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -154,17 +184,28 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # Pass 2: the same K steps with HIP events around every library call, on
-    # the stream the library launches on, for the per-kernel durations.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    d0 = [e[0].elapsed_time(e[1]) for e in evs]
-    d1 = [e[1].elapsed_time(e[2]) for e in evs]
-    avg0, avg1 = float(np.mean(d0)), float(np.mean(d1))
-    log("step: %.1f us; with events: dim0 %.1f us, dim1 %.1f us; %.0f GB/s"
+    # Pass 2: per-kernel durations with HIP events on the stream the library
+    # launches on. Each kernel runs K times back to back, with events only at
+    # the two ends of the block (an event between kernels adds a marker that
+    # costs several microseconds), alternating between the input and a copy
+    # of it so that no launch reads what the previous one left in the
+    # 256 MiB Infinity Cache.
+    x0b, x1b = x0.clone(), x1.clone()
+
+    def block_ms(fn, xa, xb):
+        a, b = HipEvent(), HipEvent()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            fn(xa if i % 2 == 0 else xb)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_ms(b) / args.steps
+
+    avg0 = block_ms(lambda x: mgs.mgs_quant_groups_dim0(x, o, False, q=q0, scales=s0), x0, x0b)
+    avg1 = block_ms(lambda x: mgs.mgs_quant_groups_dim1(x, o, False, q=q1, scales=s1), x1, x1b)
+    del x0b, x1b
+    log("step: %.1f us; kernels alone: dim0 %.1f us, dim1 %.1f us; %.0f GB/s"
         % (ms_per_step * 1e3, avg0 * 1e3, avg1 * 1e3, value))
 
     # each entry point launches one kernel here (dim0_kernel, dim1_kernel)
@@ -235,17 +276,27 @@ def _short(name):
     return None
 
 
-def rocprof_summary(d):
+def _stats_table(path):
     import csv
     out = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    stats = os.path.join(d, "trace", "run_kernel_stats.csv")
-    if os.path.exists(stats):
-        for r in csv.DictReader(open(stats)):
+    if os.path.exists(path):
+        for r in csv.DictReader(open(path)):
             k = _short(r["Name"])
             if k:
                 out.append("| %s | %s | %.2f | %.2f | %.2f |" % (
                     k, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                     float(r["MaxNs"]) / 1e3))
+    return out
+
+
+def rocprof_summary(d):
+    import csv
+    bench_stats = os.path.join(d, "bench", "run_kernel_stats.csv")
+    if os.path.exists(bench_stats):
+        print("\n".join(["## benchmark command (steps after warmup, with and without events)", ""]
+                        + _stats_table(bench_stats) + [""]))
+    out = ["## counter run (one launch at a time after a cache sweep)", ""]
+    out += _stats_table(os.path.join(d, "trace", "run_kernel_stats.csv"))
     kib = {}
     for counter in ("fetch", "write"):
         path = os.path.join(d, counter, "run_counter_collection.csv")
@@ -317,14 +368,14 @@ def timed_us(torch, fn, flush, reps=20):
     buffer (more than L2 plus the 256 MiB Infinity Cache)."""
     st = torch.cuda.current_stream()
     ts = []
+    a, b = HipEvent(), HipEvent()
     for _ in range(reps):
         flush.max()          # read-only sweep: evicts caches without leaving dirty lines
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(st)
         fn()
         b.record(st)
-        b.synchronize()
-        ts.append(a.elapsed_time(b) * 1e3)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_ms(b) * 1e3)
     return float(np.median(ts)), float(np.min(ts))
 
 
@@ -333,13 +384,13 @@ def steady_us(torch, fn, reps=20):
     each launch also pays for writing back what the one before left dirty."""
     st = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = HipEvent(), HipEvent()
     a.record(st)
     for _ in range(reps):
         fn()
     b.record(st)
-    b.synchronize()
-    return a.elapsed_time(b) * 1e3 / reps
+    torch.cuda.synchronize()
+    return a.elapsed_ms(b) * 1e3 / reps
 
 
 def per_config_table(torch, mgs, wl, dev, T, Tt):
