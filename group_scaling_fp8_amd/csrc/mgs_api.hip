@@ -23,7 +23,7 @@ int hip_status(hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Device workspace of dim0 for groups taller than 5120 rows (layout in
+// Device workspace of dim0 for groups taller than 1280 rows (layout in
 // Dim0Workspace), one per (device, stream) so that concurrent streams never
 // share it. It grows on demand and lives until process exit. gen is the last
 // generation number handed to a kernel on that stream (1 .. 2^31 - 1).
@@ -105,25 +105,47 @@ int check_grouped(const void* x, int64_t M, int64_t K, const int32_t* offsets, i
 
 namespace mgs {
 
-// Bound on a dim0 casting tile's wait for the column maxima of its group:
-// 20 ms of the device wall clock. MGS_DIM0_SPIN_TICKS overrides it (a
-// negative value skips the wait, which exercises the path that computes the
-// maxima in the casting tile itself).
-long long dim0_spin_ticks() {
-    if (const char* v = getenv("MGS_DIM0_SPIN_TICKS")) return atoll(v);
+struct DeviceInfo {
+    long long spin_ticks;   // 20 ms of the device wall clock
+    int team_max;           // min(kDim0MaxTeam, CU count)
+};
+
+DeviceInfo device_info() {
     static std::mutex mu;
-    static std::map<int, long long> per_device;
+    static std::map<int, DeviceInfo> per_device;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 2000000;
+    if (hipGetDevice(&dev) != hipSuccess) return DeviceInfo{2000000, 1};
     std::lock_guard<std::mutex> lock(mu);
     auto it = per_device.find(dev);
     if (it != per_device.end()) return it->second;
-    int khz = 0;
+    int khz = 0, cus = 0;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
         khz = 100000;
-    const long long ticks = 20LL * khz;
-    per_device[dev] = ticks;
-    return ticks;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 1;
+    DeviceInfo d{20LL * khz, cus < kDim0MaxTeam ? cus : kDim0MaxTeam};
+    per_device[dev] = d;
+    return d;
+}
+
+// Bound on a dim0 tile's wait for maxima written by other tiles: 20 ms of
+// device wall clock. MGS_DIM0_SPIN_TICKS overrides it (a negative value
+// skips the wait, which exercises the path where a tile computes the maxima
+// itself).
+long long dim0_spin_ticks(const DeviceInfo& d) {
+    if (const char* v = getenv("MGS_DIM0_SPIN_TICKS")) return atoll(v);
+    return d.spin_ticks;
+}
+
+// Most chunks of a group cast as a team: min(128, CU count).
+// MGS_DIM0_TEAM_MAX lowers it (at least 1), which sends tall groups through
+// the column-maximum tiles instead.
+int dim0_team_max(const DeviceInfo& d) {
+    if (const char* v = getenv("MGS_DIM0_TEAM_MAX")) {
+        const int t = atoi(v);
+        if (t >= 1 && t < d.team_max) return t;
+    }
+    return d.team_max;
 }
 
 }  // namespace mgs
@@ -138,7 +160,9 @@ int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* of
     if (K % 8 != 0) return MGS_ERR_INVALID_ARG;
     if (K == 0) return MGS_OK;
     if (!scales || !aligned(scales, 16)) return MGS_ERR_INVALID_ARG;
-    if (mgs::dim0_tile_bound(M, K, n_groups) >= INT32_MAX) return MGS_ERR_UNSUPPORTED;
+    const mgs::DeviceInfo dinfo = mgs::device_info();
+    const int team_max = mgs::dim0_team_max(dinfo);
+    if (mgs::dim0_tile_bound(M, K, n_groups, team_max) >= INT32_MAX) return MGS_ERR_UNSUPPORTED;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);
     void* ws = nullptr;
@@ -158,8 +182,8 @@ int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* of
     }
     return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, (int)K, offsets,
                                        n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
-                                       static_cast<uint8_t*>(q), scales, ws, gen,
-                                       mgs::dim0_spin_ticks(), s));
+                                       static_cast<uint8_t*>(q), scales, team_max, ws, gen,
+                                       mgs::dim0_spin_ticks(dinfo), s));
 }
 
 int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* offsets,

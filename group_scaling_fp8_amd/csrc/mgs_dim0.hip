@@ -17,30 +17,35 @@
 // below at 0, so any offsets array gives in-range rows.
 //
 // A 512-thread workgroup holds up to kSlabs 16-byte vectors per thread in
-// registers (160 KiB of bf16). Its tile is R rows of one group times a strip
-// of 8 * tpr columns, with tpr lanes per row:
-//   * class A, R <= 1280: one pass. tpr is the widest power of two in
-//     [16, 128] whose tile fits (short groups get strips up to 1024 columns),
-//     or 8 (64-column strips) for 641..1280 rows. Load -> column amax ->
-//     scale -> cast from registers -> store.
-//   * class B, 1280 < R <= 5120: 64-column strips; the first 1280 rows stay in
-//     registers and the rest is read twice (amax, then cast).
-//   * class C, R > 5120: chunks of at most 640 rows and 128-column strips,
-//     two tiles per (chunk, strip). Column-maximum tiles come first in the
-//     grid: each writes its chunk's column maxima to a workspace as 64-bit
-//     words, every word holding the call's generation number next to the
-//     maxima of two columns, each word one relaxed device-scope atomic store.
-//     The casting tiles come after every other tile's start; each reads the
-//     words of its strip with relaxed device-scope atomic loads until all of
-//     them carry this call's generation, combines the maxima and casts its
-//     chunk from registers (a chunk is read twice). A word is read and written
-//     whole, so the current generation implies the current maxima: no fence
-//     or flag is needed. The wait is bounded: past it the tile computes the
-//     column amax of the whole group itself, so the result never depends on
-//     the order in which workgroups run.
-// Tile order: all column-maximum tiles (group by group), then every group's
-// own tiles (class C: its casting tiles), chunk by chunk with strips fastest,
-// so workgroups that run together read neighbouring strips of the same rows.
+// registers (160 KiB of bf16), and every byte of x is loaded once into them.
+// A tile is rows of one group times a strip of 8 * tpr columns, tpr lanes
+// per row:
+//   * class A, R <= 1280 rows: one tile per strip. tpr is the widest power of
+//     two in [16, 128] whose tile fits (short groups get strips up to 1024
+//     columns), or 8 (64-column strips) for 641..1280 rows. Load -> column
+//     amax -> scale -> cast from registers -> store.
+//   * class T, R > 1280 rows and at most team_max chunks: the group is cut
+//     into c = ceil(R / 640) chunks on 128-column strips, and the c tiles of
+//     a strip are consecutive in the grid (a team). Each loads its chunk,
+//     writes the chunk's column maxima to a workspace, waits for the maxima
+//     of the other chunks of its strip, and casts its chunk from registers.
+//     team_max is at most the CU count: with two resident workgroups per CU
+//     and workgroups started in grid order, the first resident workgroups
+//     always hold a whole team, which finishes and frees room for the rest.
+//   * class C, more chunks than that: a column-maximum tile and a casting
+//     tile per (chunk, strip). All column-maximum tiles come first in the
+//     grid; a casting tile waits for its strip's maxima before its own loads,
+//     and casts its chunk (a chunk is read twice).
+// Maxima go through the workspace as 64-bit words, each holding the call's
+// generation number next to the maxima of two columns, written and read as
+// single relaxed device-scope atomics. A word is read and written whole, so
+// a reader that sees the current generation sees that call's maxima: no
+// fence or flag is needed. Every wait is bounded: past it the tile computes
+// the column amax of the whole group from x itself, so the result never
+// depends on the order in which workgroups run.
+// Tile order: all column-maximum tiles, then every group's own tiles in
+// group order: class A strip by strip; class T strip by strip with the chunks
+// of a strip together; class C chunk by chunk with strips fastest.
 #include "mgs_device.hpp"
 #include "mgs_kernels.hpp"
 
@@ -53,45 +58,44 @@ constexpr int kSlabs = kDim0Slabs;                    // vectors per thread
 constexpr int kCap = kThreads * kSlabs;               // vectors per tile
 constexpr int kRowsW64 = kCap / 8;                    // 1280 rows at 64 columns
 constexpr int kRowsW128 = kCap / 16;                  // 640 rows at 128 columns
-static_assert(kRowsW128 == kDim0HugeChunkRows, "chunk size mismatch");
-static_assert(kRowsW64 * 4 == kDim0HugeRows, "tall-group threshold mismatch");
+static_assert(kRowsW128 == kDim0ChunkRows, "chunk size mismatch");
+static_assert(kRowsW64 == kDim0TeamRows, "chunking threshold mismatch");
 static_assert((kCap >> 7) == 80 && (kCap >> 6) == 160 && (kCap >> 5) == 320,
-              "strip steps assumed by dim0_tile_bound");
+              "strip steps assumed by dim0_group_tiles");
 constexpr int kStreamSlabs = 4;                       // rows in flight per lane for streamed rows
 
-enum { kClassA = 0, kClassB = 1, kClassC = 2 };
+enum { kClassA = 0, kClassT = 1, kClassC = 2 };
 
 struct Tile {
     int g;          // group, or -1 when this workgroup has no tile
     int maxima;     // 1: class C column-maximum tile (writes no output)
-    int cls;        // kClassA / kClassB / kClassC
+    int cls;        // kClassA / kClassT / kClassC
     int lt;         // log2 of lanes per row (3..7)
     int strip;      // column strip index (strip width 8 << lt)
-    int c, nc;      // chunk index and chunk count (class C), else 0 and 1
-    int r0, r1;     // rows of this tile (the chunk for class C)
+    int c, nc;      // chunk index and chunk count (classes T, C), else 0 and 1
+    int r0, r1;     // rows of this tile (the chunk for classes T, C)
     int g0, g1;     // rows of the whole group
-    int cbase;      // class C: workspace row of the group's first chunk
+    int cbase;      // classes T, C: workspace row of the group's first chunk
 };
 
 // Per-lane view of one group: rows, class, strips, chunks and tile counts.
 struct GroupInfo {
     int start, R, lt, cls, ns, nc;
     int cnt_x;      // column-maximum tiles
-    int cnt_m;      // own tiles (class C: casting tiles)
-    int chunks;     // class C chunks
+    int cnt_m;      // own tiles
+    int chunks;     // workspace rows (classes T, C)
 };
 
-__device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, int K) {
+__device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, int K, int team_max) {
     GroupInfo gi;
     gi.start = start;
     gi.R = end - start;
     const int R = gi.R;
-    if (R > kDim0HugeRows) {
+    gi.nc = 1;
+    if (R > kRowsW64) {
         gi.lt = 4;
-        gi.cls = kClassC;
-    } else if (R > kRowsW64) {
-        gi.lt = 3;
-        gi.cls = kClassB;
+        gi.nc = (R + kRowsW128 - 1) / kRowsW128;
+        gi.cls = gi.nc <= team_max ? kClassT : kClassC;
     } else if (R > kRowsW128) {
         gi.lt = 3;
         gi.cls = kClassA;
@@ -102,9 +106,8 @@ __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, 
     // no strip wider than needed to cover K
     while (gi.lt > 3 && (8 << (gi.lt - 1)) >= K) --gi.lt;
     gi.ns = (K + (8 << gi.lt) - 1) >> (gi.lt + 3);
-    gi.nc = gi.cls == kClassC ? (R + kRowsW128 - 1) / kRowsW128 : 1;
-    gi.chunks = (valid && gi.cls == kClassC) ? gi.nc : 0;
-    gi.cnt_x = gi.chunks * gi.ns;
+    gi.chunks = (valid && gi.cls != kClassA) ? gi.nc : 0;
+    gi.cnt_x = (valid && gi.cls == kClassC) ? gi.nc * gi.ns : 0;
     gi.cnt_m = valid ? gi.nc * gi.ns : 0;
     return gi;
 }
@@ -134,11 +137,16 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
     t.cls = __builtin_amdgcn_readlane(gi.cls, src);
     t.lt = __builtin_amdgcn_readlane(gi.lt, src);
     t.nc = nc;
-    t.c = nc > 1 ? local / ns : 0;
-    t.strip = local - t.c * ns;
+    if (t.cls == kClassT) {          // the chunks of a strip together
+        t.strip = local / nc;
+        t.c = local - t.strip * nc;
+    } else {                         // strips fastest
+        t.c = local / ns;
+        t.strip = local - t.c * ns;
+    }
     t.g0 = start;
     t.g1 = start + R;
-    if (t.cls == kClassC) {
+    if (t.cls != kClassA) {
         const int cs = (R + nc - 1) / nc;
         t.r0 = min(start + t.c * cs, t.g1);
         t.r1 = min(start + (t.c + 1) * cs, t.g1);
@@ -151,7 +159,8 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
 
 // Tile number `target` of the order described at the top of this file. Run
 // by every wave of the workgroup; all lanes return the same tile.
-__device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int target) {
+__device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
+                          int target) {
     const int lane = threadIdx.x & (kWave - 1);
     Tile t;
     t.g = -1;
@@ -164,7 +173,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         int start = __shfl_up(end, 1, kWave);
         if (lane == 0) start = carry_end;
-        const GroupInfo gi = group_info(start, end, g < G, K);
+        const GroupInfo gi = group_info(start, end, g < G, K, team_max);
         const int incl_x = wave_prefix_sum_dpp(gi.cnt_x) + carry_x;
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
@@ -202,7 +211,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         int start = __shfl_up(end, 1, kWave);
         if (lane == 0) start = carry_end;
-        const GroupInfo gi = group_info(start, end, g < G, K);
+        const GroupInfo gi = group_info(start, end, g < G, K, team_max);
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
         const uint64_t hm = __ballot(gi.cnt_m > 0 && target >= incl_m - gi.cnt_m && target < incl_m);
@@ -228,7 +237,9 @@ __device__ __forceinline__ void max4(uint4& m, const uint4& t) {
 }
 
 // Column amax over every lane that shares this lane's 8 columns (same
-// tx = lane mod tpr). The result is valid in threads 0..tpr-1.
+// tx = lane mod tpr). The result is valid in threads 0..tpr-1. Ends with the
+// threads 0..tpr-1 reading red: a barrier must come before red is written
+// again.
 __device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red) {
     for (int d = tpr; d < kWave; d <<= 1) {
         m.x = mag_max2(m.x, __shfl_xor(m.x, d, kWave));
@@ -262,32 +273,30 @@ __device__ __forceinline__ TileGeom tile_geom(const Tile& t, int K) {
     return q;
 }
 
-// Loads rows [r0, r0 + nreg) of this lane's 8 columns into registers.
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t K, int r0, int nreg,
+// Loads rows [r0, r0 + nrows) of this lane's 8 columns into registers.
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t K, int r0, int nrows,
                                           const TileGeom& q, uint4 (&v)[kSlabs]) {
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
         v[s] = make_uint4(0u, 0u, 0u, 0u);
-        if (s * q.rps < nreg) {
+        if (s * q.rps < nrows) {
             const int rr = s * q.rps + q.ty;
-            if (rr < nreg && q.col_ok)
-                v[s] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
+            if (rr < nrows && q.col_ok) v[s] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
         }
     }
 }
 
-// Running column amax of rows [r0 + from, r0 + to) of this lane's columns,
+// Running column amax of rows [r0, r0 + nrows) of this lane's columns,
 // streamed through a few registers.
-__device__ __forceinline__ void stream_amax(const uint16_t* __restrict__ x, int64_t K, int r0, int from,
-                                            int to, const TileGeom& q, uint4& m) {
-    for (int base = from; base < to; base += kStreamSlabs * q.rps) {
+__device__ __forceinline__ void stream_amax(const uint16_t* __restrict__ x, int64_t K, int r0, int nrows,
+                                            const TileGeom& q, uint4& m) {
+    for (int base = 0; base < nrows; base += kStreamSlabs * q.rps) {
         uint4 u[kStreamSlabs];
 #pragma unroll
         for (int b = 0; b < kStreamSlabs; ++b) {
             u[b] = make_uint4(0u, 0u, 0u, 0u);
             const int rr = base + b * q.rps + q.ty;
-            if (rr < to && q.col_ok)
-                u[b] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
+            if (rr < nrows && q.col_ok) u[b] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
         }
 #pragma unroll
         for (int b = 0; b < kStreamSlabs; ++b) max4(m, u[b]);
@@ -302,13 +311,60 @@ __device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The words of this lane's 8 columns for chunk c of the tile's group.
+__device__ __forceinline__ uint64_t* chunk_words(uint64_t* ws_max, const Tile& t, int c, int64_t K,
+                                                 const TileGeom& q) {
+    return ws_max + (((int64_t)(t.cbase + c) * K + q.col) >> 1);
+}
+
+// Publishes this chunk's column maxima (threads 0..tpr-1 hold them).
+__device__ __forceinline__ void publish_maxima(uint64_t* ws_max, const Tile& t, int64_t K,
+                                               const TileGeom& q, uint4 m, uint32_t gen) {
+    if (threadIdx.x < q.tpr && q.col_ok) {
+        uint64_t* dst = chunk_words(ws_max, t, t.c, K, q);
+        const uint64_t g = (uint64_t)gen << 32;
+        store_agent(dst, g | m.x);
+        store_agent(dst + 1, g | m.y);
+        store_agent(dst + 2, g | m.z);
+        store_agent(dst + 3, g | m.w);
+    }
+}
+
+// Folds into m the maxima of chunks ty, ty + rps, ... of the tile's strip,
+// waiting until each word carries `gen`. Returns false if the wait ran out
+// (then m is incomplete) or was skipped (spin_ticks < 0).
+__device__ __forceinline__ bool gather_maxima(uint64_t* ws_max, const Tile& t, int64_t K,
+                                              const TileGeom& q, uint32_t gen, long long spin_ticks,
+                                              uint4& m) {
+    if (spin_ticks < 0) return false;
+    if (!q.col_ok) return true;
+    const long long t0 = wall_clock64();
+    for (int c = q.ty; c < t.nc; c += q.rps) {
+        const uint64_t* src = chunk_words(ws_max, t, c, K, q);
+        uint64_t w0, w1, w2, w3;
+        for (;;) {
+            w0 = load_agent(src);
+            w1 = load_agent(src + 1);
+            w2 = load_agent(src + 2);
+            w3 = load_agent(src + 3);
+            if ((uint32_t)(w0 >> 32) == gen && (uint32_t)(w1 >> 32) == gen &&
+                (uint32_t)(w2 >> 32) == gen && (uint32_t)(w3 >> 32) == gen)
+                break;
+            if (wall_clock64() - t0 > spin_ticks) return false;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        max4(m, make_uint4((uint32_t)w0, (uint32_t)w1, (uint32_t)w2, (uint32_t)w3));
+    }
+    return true;
+}
+
 }  // namespace
 
 // ws layout (Dim0Workspace): the epoch word, then maxima[chunk][K / 2]
 // 64-bit words (generation << 32 | two 16-bit magnitude patterns).
 __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
-        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles,
+        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max, uint32_t gen_arg,
         long long spin_ticks) {
     __shared__ uint4 red[kThreads];
@@ -316,77 +372,51 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile(off, G, M, K, (int)item);
+        const Tile t = find_tile(off, G, M, K, team_max, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);
-        const int nrows = t.r1 - t.r0;
-        const int nreg = min(nrows, geo.rps * kSlabs);     // rows held in registers
+        const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
+        const uint32_t gen = t.cls == kClassA ? 0u : (gen_arg ? gen_arg : *ws_epoch);
 
         uint4 m = make_uint4(0u, 0u, 0u, 0u);
-        if (!t.maxima && t.cls == kClassC) {
-            // casting tile of a tall group: wait, bounded, until the maxima of
-            // every chunk of this strip carry this call's generation; before
-            // the tile's own loads, so that no tile data sits in registers
-            // meanwhile. Lane (tx, ty) reads chunks ty, ty + rps, ...
-            const uint32_t gen = gen_arg ? gen_arg : *ws_epoch;
-            bool ok = spin_ticks >= 0;
-            if (ok && geo.col_ok) {
-                const long long t0 = wall_clock64();
-                for (int c = geo.ty; c < t.nc && ok; c += geo.rps) {
-                    const uint64_t* src = ws_max + (((int64_t)(t.cbase + c) * K + geo.col) >> 1);
-                    uint64_t w0, w1, w2, w3;
-                    for (;;) {
-                        w0 = load_agent(src);
-                        w1 = load_agent(src + 1);
-                        w2 = load_agent(src + 2);
-                        w3 = load_agent(src + 3);
-                        if ((uint32_t)(w0 >> 32) == gen && (uint32_t)(w1 >> 32) == gen &&
-                            (uint32_t)(w2 >> 32) == gen && (uint32_t)(w3 >> 32) == gen)
-                            break;
-                        if (wall_clock64() - t0 > spin_ticks) {
-                            ok = false;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(8);
-                    }
-                    if (ok) max4(m, make_uint4((uint32_t)w0, (uint32_t)w1, (uint32_t)w2, (uint32_t)w3));
-                }
-            }
+        if (t.cls == kClassC && !t.maxima) {
+            // casting tile of a class C group: its strip's maxima were written
+            // by tiles earlier in the grid; wait for them before the tile's own
+            // loads, so that no tile data sits in registers meanwhile
+            const bool ok = gather_maxima(ws_max, t, K, geo, gen, spin_ticks, m);
             if (!__syncthreads_and(ok)) {
-                // some maxima did not come in time: the column amax of the whole group
                 m = make_uint4(0u, 0u, 0u, 0u);
-                stream_amax(x, K, t.g0, 0, t.g1 - t.g0, geo, m);
+                stream_amax(x, K, t.g0, t.g1 - t.g0, geo, m);
             }
         }
 
         uint4 v[kSlabs];
-        load_tile(x, K, t.r0, nreg, geo, v);
+        load_tile(x, K, t.r0, nrows, geo, v);
+        if (t.cls != kClassC || t.maxima) {
+#pragma unroll
+            for (int s = 0; s < kSlabs; ++s)
+                if (s * geo.rps < nrows) max4(m, v[s]);
+        }
 
         if (t.maxima) {
             // class C column-maximum tile: publish this chunk's column maxima
-            const uint32_t gen = gen_arg ? gen_arg : *ws_epoch;
-#pragma unroll
-            for (int s = 0; s < kSlabs; ++s)
-                if (s * geo.rps < nreg) max4(m, v[s]);
             m = block_column_amax(m, geo.tpr, red);
-            if (threadIdx.x < geo.tpr && geo.col_ok) {
-                uint64_t* dst = ws_max + (((int64_t)(t.cbase + t.c) * K + geo.col) >> 1);
-                const uint64_t g = (uint64_t)gen << 32;
-                store_agent(dst, g | m.x);
-                store_agent(dst + 1, g | m.y);
-                store_agent(dst + 2, g | m.z);
-                store_agent(dst + 3, g | m.w);
-            }
+            publish_maxima(ws_max, t, K, geo, m, gen);
             __syncthreads();
             continue;     // the barrier above ends this item's reads of red
         }
-
-        if (t.cls != kClassC) {
-            // class B: rows past the register capacity are streamed for the amax
-            stream_amax(x, K, t.r0, nreg, nrows, geo, m);
-#pragma unroll
-            for (int s = 0; s < kSlabs; ++s)
-                if (s * geo.rps < nreg) max4(m, v[s]);
+        if (t.cls == kClassT) {
+            // team tile: publish this chunk's maxima, then combine the team's
+            m = block_column_amax(m, geo.tpr, red);
+            publish_maxima(ws_max, t, K, geo, m, gen);
+            m = make_uint4(0u, 0u, 0u, 0u);
+            const bool ok = gather_maxima(ws_max, t, K, geo, gen, spin_ticks, m);
+            if (!__syncthreads_and(ok)) {
+                // the team's maxima did not come in time: the column amax of
+                // the whole group from x
+                m = make_uint4(0u, 0u, 0u, 0u);
+                stream_amax(x, K, t.g0, t.g1 - t.g0, geo, m);
+            }
         }
         m = block_column_amax(m, geo.tpr, red);
 
@@ -416,28 +446,11 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
             const float s4 = ss[4], s5 = ss[5], s6 = ss[6], s7 = ss[7];
 #pragma unroll
             for (int s = 0; s < kSlabs; ++s) {
-                if (s * geo.rps < nreg) {
+                if (s * geo.rps < nrows) {
                     const int rr = s * geo.rps + geo.ty;
-                    if (rr < nreg)
-                        store_stream(q + (int64_t)(t.r0 + rr) * K + geo.col,
-                                     cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
-                }
-            }
-            // class B: second read of the streamed rows
-            for (int base = nreg; base < nrows; base += kStreamSlabs * geo.rps) {
-                uint4 u[kStreamSlabs];
-#pragma unroll
-                for (int b = 0; b < kStreamSlabs; ++b) {
-                    u[b] = make_uint4(0u, 0u, 0u, 0u);
-                    const int rr = base + b * geo.rps + geo.ty;
-                    if (rr < nrows) u[b] = load_stream(x + (int64_t)(t.r0 + rr) * K + geo.col);
-                }
-#pragma unroll
-                for (int b = 0; b < kStreamSlabs; ++b) {
-                    const int rr = base + b * geo.rps + geo.ty;
                     if (rr < nrows)
                         store_stream(q + (int64_t)(t.r0 + rr) * K + geo.col,
-                                     cast8(u[b], s0, s1, s2, s3, s4, s5, s6, s7));
+                                     cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
                 }
             }
         }
@@ -456,9 +469,9 @@ __global__ void dim0_epoch_bump_kernel(uint32_t* __restrict__ ws_epoch) {
 }
 
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, bool pow2,
-                       uint8_t* q, float* scales, void* ws, uint32_t gen, long long spin_ticks,
-                       hipStream_t stream) {
-    const int64_t n_tiles = dim0_tile_bound(M, K, G);
+                       uint8_t* q, float* scales, int team_max, void* ws, uint32_t gen,
+                       long long spin_ticks, hipStream_t stream) {
+    const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
     const int64_t grid = n_tiles < kDim0MaxGrid ? n_tiles : kDim0MaxGrid;
     const Dim0Workspace w = dim0_workspace(M, K);
@@ -466,7 +479,8 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
     const uint32_t* ws_epoch = base ? reinterpret_cast<const uint32_t*>(base + w.epoch_off) : nullptr;
     uint64_t* ws_max = base ? reinterpret_cast<uint64_t*>(base + w.max_off) : nullptr;
     hipLaunchKernelGGL(dim0_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, M, K, off,
-                       G, pow2 ? 1 : 0, q, scales, (int)n_tiles, ws_epoch, ws_max, gen, spin_ticks);
+                       G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max, ws_epoch, ws_max, gen,
+                       spin_ticks);
     return hipGetLastError();
 }
 

@@ -8,63 +8,78 @@
 namespace mgs {
 
 // dim0 tiling: 512-thread workgroups holding kDim0Slabs 16-byte vectors per
-// thread; groups taller than kDim0HugeRows are cut into chunks of at most
-// kDim0HugeChunkRows rows whose column maxima go through a workspace.
+// thread (10240 vectors, 160 KiB of bf16). A group of at most kDim0TeamRows
+// rows is one tile per column strip. A taller group is cut into chunks of at
+// most kDim0ChunkRows rows on 128-column strips: a team of chunk tiles per
+// strip when the chunk count is at most the team limit, else a
+// column-maximum tile and a casting tile per chunk and strip.
 constexpr int kDim0Slabs = 20;
-constexpr int kDim0HugeRows = 5120;
-constexpr int kDim0HugeChunkRows = 640;
+constexpr int kDim0TeamRows = 1280;
+constexpr int kDim0ChunkRows = 640;
+// Upper limit on the chunk count of a team (the library also keeps it at
+// most the CU count, so that a team fits among the resident workgroups).
+constexpr int kDim0MaxTeam = 128;
 // Largest dim0 grid launched at once; past it the workgroups loop.
 constexpr int64_t kDim0MaxGrid = int64_t(1) << 22;
 
-// Upper bound on the chunks of groups taller than kDim0HugeRows: a group of
-// s rows has ceil(s / 640) <= floor(s / 640) + 1 chunks, and there are at
-// most M / 5121 such groups.
-inline int64_t dim0_huge_chunk_bound(int64_t M) {
-    if (M <= kDim0HugeRows) return 0;
-    return M / kDim0HugeChunkRows + M / (kDim0HugeRows + 1);
+// Upper bound on the chunks of all chunked groups: a group of s > 1280 rows
+// has ceil(s / 640) <= floor(s / 640) + 1 chunks, and there are at most
+// M / 1281 such groups.
+inline int64_t dim0_chunk_bound(int64_t M) {
+    if (M <= kDim0TeamRows) return 0;
+    return M / kDim0ChunkRows + M / (kDim0TeamRows + 1);
+}
+
+// Tiles of one group of R rows (the rule of the kernel's tile search):
+// n(w) = ceil(K / w) strips of width w = 1024 columns for R <= 80, 512 up to
+// 160, 256 up to 320, 128 up to 640 and 64 up to 1280. A taller group has
+// c = ceil(R / 640) chunks on n(128) strips: c * n(128) tiles as a team
+// (c <= team_max), else 2 * c * n(128).
+inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max) {
+    auto n = [K](int64_t w) { return (K + w - 1) / w; };
+    if (R <= 80) return n(1024);
+    if (R <= 160) return n(512);
+    if (R <= 320) return n(256);
+    if (R <= 640) return n(128);
+    if (R <= kDim0TeamRows) return n(64);
+    const int64_t c = (R + kDim0ChunkRows - 1) / kDim0ChunkRows;
+    return (c <= team_max ? 1 : 2) * c * n(128);
 }
 
 // Upper bound on the dim0 tiles for any offsets, from (M, K, G) alone.
 //
-// A group of R rows gets n(w) = ceil(K / w) tiles, w being its strip width:
-// 1024 columns for R <= 80, 512 up to 160, 256 up to 320, 128 up to 640 and
-// 64 up to 5120. A taller group gets 2 * n(128) * ceil(R / 640) tiles (one
-// column-maximum tile and one casting tile per chunk and strip). So every
-// group has n(1024) tiles plus at most rho * R more, where rho is the largest
-// (tiles - n(1024)) / R over the first row count of each step (for the tall
-// groups the ratio falls as R grows, so 5121 rows is the worst). The rows of
-// all groups add up to at most M, hence
+// tiles(R) is a step function of R, so every group has n(1024) tiles plus at
+// most rho * R more, where rho is the largest (tiles(R) - n(1024)) / R over
+// the first row count R of each step with R <= M (inside a step the ratio
+// falls as R grows). The rows of all groups add up to at most M, hence
 //     tiles <= G * n(1024) + floor(rho * M).
-// No group has more tiles than one group of all M rows at its widest step
-// would have, so tiles <= G * that as well; the bound is the smaller of the
-// two.
-inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G) {
-    auto n = [K](int64_t w) { return (K + w - 1) / w; };
-    const int64_t base = n(1024);
-    const int64_t num[5] = {n(512) - base, n(256) - base, n(128) - base, n(64) - base,
-                            18 * n(128) - base};
-    const int64_t den[5] = {81, 161, 321, 641, kDim0HugeRows + 1};
-    const int steps = M > kDim0HugeRows ? 5 : 4;
+// tiles(R) never falls as R grows, so no group has more than tiles(M), and
+// tiles <= G * tiles(M) as well; the bound is the smaller of the two.
+// Team steps: rho falls with the chunk count c unless K <= 128, so all of
+// them (3 <= c <= team_max <= 128) are scanned; past team_max only the
+// first.
+inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max) {
+    const int64_t base = dim0_group_tiles(0, K, team_max);
     int64_t extra = 0;
-    for (int i = 0; i < steps; ++i) {
-        const int64_t e = M * num[i] / den[i];
+    auto step = [&](int64_t first_rows) {
+        if (first_rows > M) return;
+        const int64_t num = dim0_group_tiles(first_rows, K, team_max) - base;
+        const int64_t e = M * num / first_rows;
         if (e > extra) extra = e;
-    }
-    // most tiles of a single group of at most M rows
-    int64_t one = base;
-    const int64_t first_rows[4] = {81, 161, 321, 641};
-    const int64_t step_tiles[4] = {n(512), n(256), n(128), n(64)};
-    for (int i = 0; i < 4; ++i)
-        if (M >= first_rows[i] && step_tiles[i] > one) one = step_tiles[i];
-    if (M > kDim0HugeRows) {
-        const int64_t tall = 2 * n(128) * ((M + kDim0HugeChunkRows - 1) / kDim0HugeChunkRows);
-        if (tall > one) one = tall;
-    }
+    };
+    step(81);
+    step(161);
+    step(321);
+    step(641);
+    // chunked groups have at least 3 chunks (more than 1280 rows)
+    const int64_t last = team_max + 1 > 3 ? team_max + 1 : 3;
+    for (int64_t c = 3; c <= last; ++c) step(kDim0ChunkRows * (c - 1) + 1);
     const int64_t spread = G * base + extra;
-    return spread < G * one ? spread : G * one;
+    const int64_t one = G * dim0_group_tiles(M, K, team_max);
+    return spread < one ? spread : one;
 }
 
-// dim0 workspace (needed only when M > kDim0HugeRows), 256-byte aligned
+// dim0 workspace (needed only when M > kDim0TeamRows), 256-byte aligned
 // regions: an epoch word, then the column maxima of every chunk, one 64-bit
 // word per column pair (generation << 32 | two 16-bit magnitude patterns).
 struct Dim0Workspace {
@@ -74,7 +89,7 @@ struct Dim0Workspace {
 
 inline Dim0Workspace dim0_workspace(int64_t M, int64_t K) {
     Dim0Workspace w;
-    w.chunks = dim0_huge_chunk_bound(M);
+    w.chunks = dim0_chunk_bound(M);
     w.epoch_off = 0;
     w.max_off = 256;
     w.bytes = w.max_off + (size_t)(w.chunks * (K / 2)) * sizeof(uint64_t);

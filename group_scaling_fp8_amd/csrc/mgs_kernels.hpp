@@ -8,15 +8,16 @@
 
 namespace mgs {
 
-// gen != 0: the generation that this call's column-maximum tiles write.
-// gen == 0: the generation is read from the workspace's epoch word, which
-// launch_dim0_epoch_bump advances in stream order (for graph replays).
-// spin_ticks bounds the wait of a casting tile for its column maxima, in
-// wall-clock ticks; past it the tile computes them itself. A negative value
-// skips the wait.
+// team_max: the most chunks a group may have to be cast as a team (at most
+// the CU count, see mgs_dim0.hip). gen != 0: the generation number this
+// call's maxima words carry. gen == 0: the generation is read from the
+// workspace's epoch word, which launch_dim0_epoch_bump advances in stream
+// order (for graph replays). spin_ticks bounds a tile's wait for maxima
+// written by other tiles, in device wall-clock ticks; past it the tile
+// computes them itself. A negative value skips the wait.
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, bool pow2,
-                       uint8_t* q, float* scales, void* ws, uint32_t gen, long long spin_ticks,
-                       hipStream_t stream);
+                       uint8_t* q, float* scales, int team_max, void* ws, uint32_t gen,
+                       long long spin_ticks, hipStream_t stream);
 
 hipError_t launch_dim0_epoch_bump(void* ws, hipStream_t stream);
 

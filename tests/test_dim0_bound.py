@@ -5,8 +5,9 @@ alone, so the bound must hold for every way of splitting M rows into G
 groups. The tile count of a group depends only on its row count, as a step
 function, so the worst split is found exactly by a knapsack over the first
 row count of each step (0, 81, 161, 321, 641, then 640 * (c - 1) + 1 for the
-chunked groups). The C++ bound, compiled with g++ from the header the library
-uses, must be at least that worst case."""
+groups cut into c chunks). The C++ bound, compiled with g++ from the header
+the library uses, must be at least that worst case, for several team
+limits (the most chunks a group may have to be cast as a team)."""
 import math
 import os
 import subprocess
@@ -22,34 +23,36 @@ DRIVER = r"""
 #include <stdio.h>
 #include "mgs_dim0_layout.hpp"
 int main() {
-    long long M, K, G;
-    while (scanf("%lld %lld %lld", &M, &K, &G) == 3)
-        printf("%lld %lld\n", (long long)mgs::dim0_tile_bound(M, K, G),
-               (long long)mgs::dim0_huge_chunk_bound(M));
+    long long M, K, G, T;
+    while (scanf("%lld %lld %lld %lld", &M, &K, &G, &T) == 4)
+        printf("%lld %lld %lld\n", (long long)mgs::dim0_tile_bound(M, K, G, T),
+               (long long)mgs::dim0_chunk_bound(M), (long long)mgs::dim0_group_tiles(M, K, T));
     return 0;
 }
 """
 
 
-def tiles(R, K):
-    """Tiles of one group of R rows (the rule the kernel's tile search uses)."""
-    if R > 5120:
-        lt, chunked = 4, True
+def tiles(R, K, team_max):
+    """Tiles of one group of R rows (the rule of the kernel's tile search)."""
+    if R > 1280:
+        lt, chunks = 4, -(-R // 640)
     elif R > 640:
-        lt, chunked = 3, False
+        lt, chunks = 3, 0
     else:
         lt = 7 if R <= 80 else 6 if R <= 160 else 5 if R <= 320 else 4
-        chunked = False
+        chunks = 0
     while lt > 3 and (8 << (lt - 1)) >= K:
         lt -= 1
     ns = -(-K // (8 << lt))
-    return 2 * ns * -(-R // 640) if chunked else ns
+    if chunks == 0:
+        return ns
+    return (1 if chunks <= team_max else 2) * chunks * ns
 
 
-def worst_splits(Mmax, K, Gmax):
+def worst_splits(Mmax, K, Gmax, team_max):
     """best[G][M] = the most tiles over all splits of at most M rows into
     exactly G groups."""
-    sizes = [0, 81, 161, 321, 641] + [640 * (c - 1) + 1 for c in range(9, Mmax // 640 + 3)]
+    sizes = [0, 81, 161, 321, 641] + [640 * (c - 1) + 1 for c in range(3, Mmax // 640 + 3)]
     sizes = [r for r in sizes if r <= Mmax]
     NEG = -(1 << 40)
     dp = np.full(Mmax + 1, NEG, np.int64)
@@ -58,7 +61,7 @@ def worst_splits(Mmax, K, Gmax):
     for _ in range(Gmax):
         nxt = np.full(Mmax + 1, NEG, np.int64)
         for r in sizes:
-            t = tiles(r, K)
+            t = tiles(r, K, team_max)
             np.maximum(nxt[r:], dp[:Mmax + 1 - r] + t, out=nxt[r:])
         dp = nxt
         best.append(np.maximum.accumulate(dp))
@@ -75,40 +78,42 @@ def bound_tool():
     subprocess.run(["g++", "-O1", "-std=c++17", "-I", CSRC, "-o", exe, src], check=True)
 
     def run(triples):
-        inp = "".join("%d %d %d\n" % t for t in triples)
+        inp = "".join("%d %d %d %d\n" % t for t in triples)
         out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
         return [tuple(int(v) for v in line.split()) for line in out.splitlines()]
     return run
 
 
+@pytest.mark.parametrize("team_max", [1, 3, 26, 128])
 @pytest.mark.parametrize("K", [8, 64, 72, 136, 1032, 8192])
-def test_bound_covers_the_worst_split(bound_tool, K):
+def test_bound_covers_the_worst_split(bound_tool, K, team_max):
     Mmax, Gmax = 17000, 64
-    best = worst_splits(Mmax, K, Gmax)
-    Ms = [0, 1, 80, 81, 400, 641, 1300, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
+    best = worst_splits(Mmax, K, Gmax, team_max)
+    Ms = [0, 1, 80, 81, 400, 641, 1280, 1281, 1921, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
     Gs = [1, 2, 3, 7, 16, 64]
-    triples = [(M, K, G) for M in Ms for G in Gs]
+    triples = [(M, K, G, team_max) for M in Ms for G in Gs]
     got = bound_tool(triples)
-    for (M, _, G), (b, _) in zip(triples, got):
+    for (M, _, G, _), (b, _, one) in zip(triples, got):
         exact = int(best[G][M])
-        assert b >= exact, (M, K, G, b, exact)
+        assert b >= exact, (M, K, G, team_max, b, exact)
         # and it is no wild over-estimate (the grid's extra workgroups exit at once)
-        assert b <= 2 * exact + 16, (M, K, G, b, exact)
+        assert b <= 2 * exact + 16, (M, K, G, team_max, b, exact)
+        assert one == tiles(M, K, team_max)
 
 
 def test_bound_of_the_benchmark_shape(bound_tool):
-    (b, chunks), = bound_tool([(16640, 8192, 64)])
-    exact = int(worst_splits(16640, 8192, 64)[64][16640])
-    assert exact <= b == 4229
-    assert chunks == 16640 // 640 + 16640 // 5121
+    (b, chunks, _), = bound_tool([(16640, 8192, 64, 128)])
+    exact = int(worst_splits(16640, 8192, 64, 128)[64][16640])
+    assert exact <= b
+    assert chunks == 16640 // 640 + 16640 // 1281
 
 
 def test_chunk_bound_covers_every_chunked_split(bound_tool):
-    # the chunked groups of any split have at most dim0_huge_chunk_bound(M) chunks
-    for M in (5121, 5760, 5761, 10242, 10243, 16640, 40000):
-        (_, chunks), = bound_tool([(M, 8, 1)])
+    # the chunked groups of any split have at most dim0_chunk_bound(M) chunks
+    for M in (1281, 1920, 1921, 2562, 5121, 10242, 10243, 16640, 40000):
+        (_, chunks, _), = bound_tool([(M, 8, 1, 128)])
         worst = 0
-        for n in range(1, M // 5121 + 1):           # n groups of just over 5120 rows
+        for n in range(1, M // 1281 + 1):           # n groups of just over 1280 rows
             rows = M // n
             worst = max(worst, n * math.ceil(rows / 640))
         assert chunks >= worst, (M, chunks, worst)

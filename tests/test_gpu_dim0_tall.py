@@ -1,9 +1,12 @@
 """GPU parity of dim0 where the launch shape matters: the group sizes that
 give the most tiles per row (the grid is an upper bound computed from M, K
-and G alone), groups taller than 5120 rows whose column maxima pass between
-workgroups of one launch, the path that computes those maxima in the casting
-tile itself (forced from the host by a negative wait bound), back-to-back
-calls on one stream and on two, and replays of a captured graph."""
+and G alone), groups taller than 1280 rows whose column maxima pass between
+workgroups of one launch (as a team of chunk tiles, or through
+column-maximum tiles when a group has more chunks than the team limit,
+forced low here through MGS_DIM0_TEAM_MAX), the path that computes those
+maxima from x in the waiting tile itself (forced from the host by a
+negative wait bound), back-to-back calls on one stream and on two, and
+replays of a captured graph."""
 import os
 
 import numpy as np
@@ -46,17 +49,35 @@ def data(seed, M, K):
     return wl.randn_bf16(np.random.default_rng(seed), (M, K), 0.02, 0.003, 8.0)
 
 
+TEAM_MAX = [None, "1"]      # the library's limit, then every tall group through maxima tiles
+
+
+def team_env(monkeypatch, team_max):
+    if team_max is None:
+        monkeypatch.delenv("MGS_DIM0_TEAM_MAX", raising=False)
+    else:
+        monkeypatch.setenv("MGS_DIM0_TEAM_MAX", team_max)
+
+
 # The first row count of each tiling step has the most tiles per row: 81 rows
-# (512-column strips), 161 (256), 321 (128), 641 (64), 5121 (chunked, two
-# tiles per chunk and strip). K values leave a ragged last strip.
+# (512-column strips), 161 (256), 321 (128), 641 (64), then 640 * (c - 1) + 1
+# rows for a group cut into c chunks. K values leave a ragged last strip.
+@pytest.mark.parametrize("team_max", TEAM_MAX)
 @pytest.mark.parametrize("size,n,K", [
-    (81, 12, 2056), (161, 12, 1032), (321, 10, 520), (641, 8, 264), (5121, 2, 264),
-    (5121, 3, 72), (5761, 2, 136),
+    (81, 12, 2056), (161, 12, 1032), (321, 10, 520), (641, 8, 264), (1281, 4, 264),
+    (1921, 3, 136), (5121, 2, 264), (5121, 3, 72),
 ])
-def test_most_tiles_per_row(size, n, K):
+def test_most_tiles_per_row(size, n, K, team_max, monkeypatch):
+    team_env(monkeypatch, team_max)
     off = (np.arange(1, n + 1) * size).astype(np.int32)
     x = data(size + n, size * n, K)
     check(x, off, "groups of %d rows" % size)
+
+
+def test_group_past_the_team_limit():
+    # 141 chunks, more than any team: column-maximum tiles, then casting tiles
+    M, K = 90000, 64
+    check(data(9, M, K), np.array([5, M - 7, M], np.int32), "90000-row group")
 
 
 def test_many_groups_at_the_group_limit():
@@ -66,12 +87,15 @@ def test_many_groups_at_the_group_limit():
     check(data(7, int(off[-1]), 8), off, "1024 groups")
 
 
+@pytest.mark.parametrize("team_max", TEAM_MAX)
 @pytest.mark.parametrize("M,K,sizes", [
     (12000, 136, [0, 11000, 1000]),
     (16640, 256, [16640]),
     (11000, 64, [5500, 5500]),
+    (3000, 520, [1281, 1719]),
 ])
-def test_tall_groups_without_the_wait(M, K, sizes, monkeypatch):
+def test_tall_groups_without_the_wait(M, K, sizes, team_max, monkeypatch):
+    team_env(monkeypatch, team_max)
     off = np.cumsum(sizes).astype(np.int32)
     x = data(M + K, M, K)
     monkeypatch.setenv("MGS_DIM0_SPIN_TICKS", "-1")
@@ -80,7 +104,9 @@ def test_tall_groups_without_the_wait(M, K, sizes, monkeypatch):
     check(x, off, "zero wait %s" % (sizes,))
 
 
-def test_back_to_back_tall_calls_on_one_stream_and_two():
+@pytest.mark.parametrize("team_max", TEAM_MAX)
+def test_back_to_back_tall_calls_on_one_stream_and_two(team_max, monkeypatch):
+    team_env(monkeypatch, team_max)
     M, K = 13000, 264
     off = np.array([300, 12000, 13000], np.int32)
     xs = [data(20 + i, M, K) for i in range(3)]
@@ -104,7 +130,9 @@ def test_back_to_back_tall_calls_on_one_stream_and_two():
     assert_same_bytes(other[1].cpu().numpy(), rs, "side stream scales")
 
 
-def test_graph_replays_of_a_tall_group():
+@pytest.mark.parametrize("team_max", TEAM_MAX)
+def test_graph_replays_of_a_tall_group(team_max, monkeypatch):
+    team_env(monkeypatch, team_max)
     M, K = 11000, 136
     off = np.array([200, 10600, 11000], np.int32)
     xs = [data(40 + i, M, K) for i in range(3)]
