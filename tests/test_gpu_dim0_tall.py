@@ -65,7 +65,8 @@ def team_env(monkeypatch, team_max):
 @pytest.mark.parametrize("team_max", TEAM_MAX)
 @pytest.mark.parametrize("size,n,K", [
     (81, 12, 2056), (161, 12, 1032), (321, 10, 520), (641, 8, 264), (1281, 4, 264),
-    (1921, 3, 136), (5121, 2, 264), (5121, 3, 72),
+    (1921, 3, 136), (5121, 2, 264), (5121, 3, 72), (37, 16, 4104), (577, 4, 264),
+    (865, 3, 136),
 ])
 def test_most_tiles_per_row(size, n, K, team_max, monkeypatch):
     team_env(monkeypatch, team_max)

@@ -216,7 +216,8 @@ def edge_values(rng, shape):
     (12000, 136, [0, 11000, 1000]),              # a group cut into chunks (maxima through the workspace)
     (7000, 512, [5121, 1279, 600]),              # a chunked group next to one just under the threshold
     (6000, 64, [5120, 880]),                     # chunked, with 64-column rows
-    (2600, 264, [1280, 1281, 39]),               # either side of the chunking threshold
+    (2600, 264, [1280, 1281, 39]),               # two chunked groups and a short one
+    (1300, 264, [576, 577, 147]),                # either side of the chunking threshold
 ])
 def test_dim0_edges(M, K, sizes, pow2):
     rng = np.random.default_rng(M * 7 + K)
