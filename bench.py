@@ -423,7 +423,7 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
     tall = [
         # every row in one group: 26 chunks of 640 rows (column maxima through the workspace)
         wl.Workload("dim0 (16640,8192) G=1", "dim0", T, np.array([M], dtype=np.int32)),
-        # eight groups of 2080 rows: 64-column strips, rows past 1280 read twice
+        # eight groups of 2080 rows: teams of four 520-row chunks
         wl.Workload("dim0 (16640,8192) G=8 even", "dim0", T,
                     np.arange(1, 9, dtype=np.int32) * (M // 8)),
     ]

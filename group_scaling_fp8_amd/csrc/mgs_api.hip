@@ -23,7 +23,7 @@ int hip_status(hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Device workspace of dim0 for groups taller than 1280 rows (layout in
+// Device workspace of dim0 for groups taller than 640 rows (layout in
 // Dim0Workspace), one per (device, stream) so that concurrent streams never
 // share it. It grows on demand and lives until process exit. gen is the last
 // generation number handed to a kernel on that stream (1 .. 2^31 - 1).

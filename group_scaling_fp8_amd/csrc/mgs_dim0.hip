@@ -20,11 +20,12 @@
 // registers (160 KiB of bf16), and every byte of x is loaded once into them.
 // A tile is rows of one group times a strip of 8 * tpr columns, tpr lanes
 // per row:
-//   * class A, R <= 1280 rows: one tile per strip. tpr is the widest power of
+//   * class A, R <= 640 rows: one tile per strip. tpr is the widest power of
 //     two in [16, 128] whose tile fits (short groups get strips up to 1024
-//     columns), or 8 (64-column strips) for 641..1280 rows. Load -> column
-//     amax -> scale -> cast from registers -> store.
-//   * class T, R > 1280 rows and at most team_max chunks: the group is cut
+//     columns). Load -> column amax -> scale -> cast from registers -> store.
+//     No strip is narrower than 128 columns unless K is: rows of 128 bytes
+//     stream far worse than rows of 256.
+//   * class T, R > 640 rows and at most team_max chunks: the group is cut
 //     into c = ceil(R / 640) chunks on 128-column strips, and the c tiles of
 //     a strip are consecutive in the grid (a team). Each loads its chunk,
 //     writes the chunk's column maxima to a workspace, waits for the maxima
@@ -56,10 +57,9 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kSlabs = kDim0Slabs;                    // vectors per thread
 constexpr int kCap = kThreads * kSlabs;               // vectors per tile
-constexpr int kRowsW64 = kCap / 8;                    // 1280 rows at 64 columns
 constexpr int kRowsW128 = kCap / 16;                  // 640 rows at 128 columns
 static_assert(kRowsW128 == kDim0ChunkRows, "chunk size mismatch");
-static_assert(kRowsW64 == kDim0TeamRows, "chunking threshold mismatch");
+static_assert(kRowsW128 == kDim0TeamRows, "chunking threshold mismatch");
 static_assert((kCap >> 7) == 80 && (kCap >> 6) == 160 && (kCap >> 5) == 320,
               "strip steps assumed by dim0_group_tiles");
 constexpr int kStreamSlabs = 4;                       // rows in flight per lane for streamed rows
@@ -92,13 +92,10 @@ __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, 
     gi.R = end - start;
     const int R = gi.R;
     gi.nc = 1;
-    if (R > kRowsW64) {
+    if (R > kRowsW128) {
         gi.lt = 4;
         gi.nc = (R + kRowsW128 - 1) / kRowsW128;
         gi.cls = gi.nc <= team_max ? kClassT : kClassC;
-    } else if (R > kRowsW128) {
-        gi.lt = 3;
-        gi.cls = kClassA;
     } else {
         gi.lt = R <= (kCap >> 7) ? 7 : (R <= (kCap >> 6) ? 6 : (R <= (kCap >> 5) ? 5 : 4));
         gi.cls = kClassA;

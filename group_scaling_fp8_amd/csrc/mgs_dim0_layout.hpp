@@ -14,7 +14,7 @@ namespace mgs {
 // strip when the chunk count is at most the team limit, else a
 // column-maximum tile and a casting tile per chunk and strip.
 constexpr int kDim0Slabs = 20;
-constexpr int kDim0TeamRows = 1280;
+constexpr int kDim0TeamRows = 640;
 constexpr int kDim0ChunkRows = 640;
 // Upper limit on the chunk count of a team (the library also keeps it at
 // most the CU count, so that a team fits among the resident workgroups).
@@ -22,9 +22,9 @@ constexpr int kDim0MaxTeam = 128;
 // Largest dim0 grid launched at once; past it the workgroups loop.
 constexpr int64_t kDim0MaxGrid = int64_t(1) << 22;
 
-// Upper bound on the chunks of all chunked groups: a group of s > 1280 rows
+// Upper bound on the chunks of all chunked groups: a group of s > 640 rows
 // has ceil(s / 640) <= floor(s / 640) + 1 chunks, and there are at most
-// M / 1281 such groups.
+// M / 641 such groups.
 inline int64_t dim0_chunk_bound(int64_t M) {
     if (M <= kDim0TeamRows) return 0;
     return M / kDim0ChunkRows + M / (kDim0TeamRows + 1);
@@ -32,16 +32,15 @@ inline int64_t dim0_chunk_bound(int64_t M) {
 
 // Tiles of one group of R rows (the rule of the kernel's tile search):
 // n(w) = ceil(K / w) strips of width w = 1024 columns for R <= 80, 512 up to
-// 160, 256 up to 320, 128 up to 640 and 64 up to 1280. A taller group has
-// c = ceil(R / 640) chunks on n(128) strips: c * n(128) tiles as a team
-// (c <= team_max), else 2 * c * n(128).
+// 160, 256 up to 320 and 128 up to 640. A taller group has c = ceil(R / 640)
+// chunks on n(128) strips: c * n(128) tiles as a team (c <= team_max), else
+// 2 * c * n(128).
 inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max) {
     auto n = [K](int64_t w) { return (K + w - 1) / w; };
     if (R <= 80) return n(1024);
     if (R <= 160) return n(512);
     if (R <= 320) return n(256);
     if (R <= 640) return n(128);
-    if (R <= kDim0TeamRows) return n(64);
     const int64_t c = (R + kDim0ChunkRows - 1) / kDim0ChunkRows;
     return (c <= team_max ? 1 : 2) * c * n(128);
 }
@@ -56,7 +55,7 @@ inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max) {
 // tiles(R) never falls as R grows, so no group has more than tiles(M), and
 // tiles <= G * tiles(M) as well; the bound is the smaller of the two.
 // Team steps: rho falls with the chunk count c unless K <= 128, so all of
-// them (3 <= c <= team_max <= 128) are scanned; past team_max only the
+// them (2 <= c <= team_max <= 128) are scanned; past team_max only the
 // first.
 inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max) {
     const int64_t base = dim0_group_tiles(0, K, team_max);
@@ -70,10 +69,9 @@ inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max
     step(81);
     step(161);
     step(321);
-    step(641);
-    // chunked groups have at least 3 chunks (more than 1280 rows)
-    const int64_t last = team_max + 1 > 3 ? team_max + 1 : 3;
-    for (int64_t c = 3; c <= last; ++c) step(kDim0ChunkRows * (c - 1) + 1);
+    // chunked groups have at least 2 chunks (more than 640 rows)
+    const int64_t last = team_max + 1 > 2 ? team_max + 1 : 2;
+    for (int64_t c = 2; c <= last; ++c) step(kDim0ChunkRows * (c - 1) + 1);
     const int64_t spread = G * base + extra;
     const int64_t one = G * dim0_group_tiles(M, K, team_max);
     return spread < one ? spread : one;

@@ -73,9 +73,9 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * Requirements: M >= 0, K >= 0, K % 8 == 0; x 16-byte aligned, q 8-byte
  * aligned, scales 16-byte aligned. M == 0 writes only the scales; K == 0 is a
  * no-op.
- * Memory: when M > 1280, a group taller than 1280 rows is cut into chunks of
+ * Memory: when M > 640, a group taller than 640 rows is cut into chunks of
  * at most 640 rows. Each chunk's column maxima go through a device workspace
- * of about (M / 427) * K * 4 bytes, between workgroups of the one kernel
+ * of about (M / 320) * K * 4 bytes, between workgroups of the one kernel
  * launch. A tile that waits for other tiles' maxima waits at most about
  * 20 ms of device wall clock; past that it computes them from x itself, so
  * the result never depends on workgroup scheduling. Two environment
@@ -88,7 +88,7 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * The library allocates the workspace once per (device, stream)
  * with hipMalloc, zeroes it, grows it as needed, and frees it only at process
  * exit. Graph capture: a call on a capturing stream adds one single-thread
- * kernel before the main one and replays correctly. When M > 1280 it needs
+ * kernel before the main one and replays correctly. When M > 640 it needs
  * the workspace to exist already, so make one call of at least that size
  * eagerly on the same stream first. Otherwise it returns
  * MGS_ERR_UNSUPPORTED. Replays use the capturing stream's workspace, so they

@@ -4,9 +4,9 @@ The dim0 launch has one workgroup per tile and sizes its grid from (M, K, G)
 alone, so the bound must hold for every way of splitting M rows into G
 groups. The tile count of a group depends only on its row count, as a step
 function, so the worst split is found exactly by a knapsack over the first
-row count of each step (0, 81, 161, 321, 641, then 640 * (c - 1) + 1 for the
-groups cut into c chunks). The C++ bound, compiled with g++ from the header
-the library uses, must be at least that worst case, for several team
+row count of each step (0, 81, 161, 321, then 640 * (c - 1) + 1 for the
+groups cut into c >= 2 chunks). The C++ bound, compiled with g++ from the
+header the library uses, must be at least that worst case, for several team
 limits (the most chunks a group may have to be cast as a team)."""
 import math
 import os
@@ -34,10 +34,8 @@ int main() {
 
 def tiles(R, K, team_max):
     """Tiles of one group of R rows (the rule of the kernel's tile search)."""
-    if R > 1280:
+    if R > 640:
         lt, chunks = 4, -(-R // 640)
-    elif R > 640:
-        lt, chunks = 3, 0
     else:
         lt = 7 if R <= 80 else 6 if R <= 160 else 5 if R <= 320 else 4
         chunks = 0
@@ -52,7 +50,7 @@ def tiles(R, K, team_max):
 def worst_splits(Mmax, K, Gmax, team_max):
     """best[G][M] = the most tiles over all splits of at most M rows into
     exactly G groups."""
-    sizes = [0, 81, 161, 321, 641] + [640 * (c - 1) + 1 for c in range(3, Mmax // 640 + 3)]
+    sizes = [0, 81, 161, 321] + [640 * (c - 1) + 1 for c in range(2, Mmax // 640 + 3)]
     sizes = [r for r in sizes if r <= Mmax]
     NEG = -(1 << 40)
     dp = np.full(Mmax + 1, NEG, np.int64)
@@ -89,7 +87,7 @@ def bound_tool():
 def test_bound_covers_the_worst_split(bound_tool, K, team_max):
     Mmax, Gmax = 17000, 64
     best = worst_splits(Mmax, K, Gmax, team_max)
-    Ms = [0, 1, 80, 81, 400, 641, 1280, 1281, 1921, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
+    Ms = [0, 1, 80, 81, 400, 640, 641, 1280, 1281, 1921, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
     Gs = [1, 2, 3, 7, 16, 64]
     triples = [(M, K, G, team_max) for M in Ms for G in Gs]
     got = bound_tool(triples)
@@ -105,15 +103,15 @@ def test_bound_of_the_benchmark_shape(bound_tool):
     (b, chunks, _), = bound_tool([(16640, 8192, 64, 128)])
     exact = int(worst_splits(16640, 8192, 64, 128)[64][16640])
     assert exact <= b
-    assert chunks == 16640 // 640 + 16640 // 1281
+    assert chunks == 16640 // 640 + 16640 // 641
 
 
 def test_chunk_bound_covers_every_chunked_split(bound_tool):
     # the chunked groups of any split have at most dim0_chunk_bound(M) chunks
-    for M in (1281, 1920, 1921, 2562, 5121, 10242, 10243, 16640, 40000):
+    for M in (641, 1281, 1282, 1920, 1921, 2562, 5121, 10242, 10243, 16640, 40000):
         (_, chunks, _), = bound_tool([(M, 8, 1, 128)])
         worst = 0
-        for n in range(1, M // 1281 + 1):           # n groups of just over 1280 rows
+        for n in range(1, M // 641 + 1):            # n groups of just over 640 rows
             rows = M // n
             worst = max(worst, n * math.ceil(rows / 640))
         assert chunks >= worst, (M, chunks, worst)

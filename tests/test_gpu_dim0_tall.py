@@ -1,6 +1,6 @@
 """GPU parity of dim0 where the launch shape matters: the group sizes that
 give the most tiles per row (the grid is an upper bound computed from M, K
-and G alone), groups taller than 1280 rows whose column maxima pass between
+and G alone), groups taller than 640 rows whose column maxima pass between
 workgroups of one launch (as a team of chunk tiles, or through
 column-maximum tiles when a group has more chunks than the team limit,
 forced low here through MGS_DIM0_TEAM_MAX), the path that computes those
@@ -60,13 +60,13 @@ def team_env(monkeypatch, team_max):
 
 
 # The first row count of each tiling step has the most tiles per row: 81 rows
-# (512-column strips), 161 (256), 321 (128), 641 (64), then 640 * (c - 1) + 1
-# rows for a group cut into c chunks. K values leave a ragged last strip.
+# (512-column strips), 161 (256), 321 (128), then 640 * (c - 1) + 1 rows for a
+# group cut into c chunks (641: two). K values leave a ragged last strip.
 @pytest.mark.parametrize("team_max", TEAM_MAX)
 @pytest.mark.parametrize("size,n,K", [
     (81, 12, 2056), (161, 12, 1032), (321, 10, 520), (641, 8, 264), (1281, 4, 264),
     (1921, 3, 136), (5121, 2, 264), (5121, 3, 72), (37, 16, 4104), (577, 4, 264),
-    (865, 3, 136),
+    (865, 3, 136), (640, 5, 264), (1280, 3, 136),
 ])
 def test_most_tiles_per_row(size, n, K, team_max, monkeypatch):
     team_env(monkeypatch, team_max)
@@ -94,6 +94,7 @@ def test_many_groups_at_the_group_limit():
     (16640, 256, [16640]),
     (11000, 64, [5500, 5500]),
     (3000, 520, [1281, 1719]),
+    (2000, 264, [641, 700, 659]),
 ])
 def test_tall_groups_without_the_wait(M, K, sizes, team_max, monkeypatch):
     team_env(monkeypatch, team_max)

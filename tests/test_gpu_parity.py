@@ -211,13 +211,14 @@ def edge_values(rng, shape):
     (512, 256, [512]),                           # exactly one chunk
     (513, 136, [513]),                           # just taller than one chunk
     (1500, 128, [0, 1024, 3, 473]),              # tall group next to tiny ones
-    (2000, 384, [700, 0, 0, 1300]),              # 64-column strips, and one group read twice
+    (2000, 384, [700, 0, 0, 1300]),              # two- and three-chunk teams around empty groups
     (96, 64, [32, 32, 32]),
     (12000, 136, [0, 11000, 1000]),              # a group cut into chunks (maxima through the workspace)
-    (7000, 512, [5121, 1279, 600]),              # a chunked group next to one just under the threshold
+    (7000, 512, [5121, 1279, 600]),              # chunked groups next to one just under the threshold
     (6000, 64, [5120, 880]),                     # chunked, with 64-column rows
     (2600, 264, [1280, 1281, 39]),               # two chunked groups and a short one
-    (1300, 264, [576, 577, 147]),                # either side of the chunking threshold
+    (1300, 264, [576, 577, 147]),                # 128-column strips with a ragged last slab
+    (1300, 264, [640, 641, 19]),                 # either side of the chunking threshold
 ])
 def test_dim0_edges(M, K, sizes, pow2):
     rng = np.random.default_rng(M * 7 + K)
