@@ -234,9 +234,10 @@ __device__ __forceinline__ void max4(uint4& m, const uint4& t) {
 }
 
 // Column amax over every lane that shares this lane's 8 columns (same
-// tx = lane mod tpr). The result is valid in threads 0..tpr-1. Ends with the
-// threads 0..tpr-1 reading red: a barrier must come before red is written
-// again.
+// tx = lane mod tpr), returned in every lane: xor shuffles inside the wave,
+// then one partial per (wave, tx) through LDS (per (row, tx) when a row spans
+// waves) and one barrier. Ends with every thread reading red: a barrier must
+// come before red is written again.
 __device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red) {
     for (int d = tpr; d < kWave; d <<= 1) {
         m.x = mag_max2(m.x, __shfl_xor(m.x, d, kWave));
@@ -244,13 +245,19 @@ __device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red)
         m.z = mag_max2(m.z, __shfl_xor(m.z, d, kWave));
         m.w = mag_max2(m.w, __shfl_xor(m.w, d, kWave));
     }
-    red[threadIdx.x] = m;
-    __syncthreads();
-    uint4 a = make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x < tpr) {
-        const int stride = tpr > kWave ? tpr : kWave;
-        for (int k = threadIdx.x; k < kThreads; k += stride) max4(a, red[k]);
+    const int lane = threadIdx.x & (kWave - 1);
+    int parts;
+    if (tpr <= kWave) {
+        parts = kThreads / kWave;
+        if (lane < tpr) red[(threadIdx.x / kWave) * tpr + lane] = m;
+    } else {
+        parts = kThreads / tpr;
+        red[threadIdx.x] = m;
     }
+    __syncthreads();
+    const int tx = threadIdx.x & (tpr - 1);
+    uint4 a = make_uint4(0u, 0u, 0u, 0u);
+    for (int p = 0; p < parts; ++p) max4(a, red[p * tpr + tx]);
     return a;
 }
 
@@ -365,7 +372,6 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max, uint32_t gen_arg,
         long long spin_ticks) {
     __shared__ uint4 red[kThreads];
-    __shared__ float s_scale[128 * 8];
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
@@ -417,30 +423,18 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         }
         m = block_column_amax(m, geo.tpr, red);
 
-        if (threadIdx.x < geo.tpr) {
-            const bool p2 = pow2 != 0;
-            float s[8];
-            s[0] = group_scale(m.x & 0xFFFFu, p2);
-            s[1] = group_scale(m.x >> 16, p2);
-            s[2] = group_scale(m.y & 0xFFFFu, p2);
-            s[3] = group_scale(m.y >> 16, p2);
-            s[4] = group_scale(m.z & 0xFFFFu, p2);
-            s[5] = group_scale(m.z >> 16, p2);
-            s[6] = group_scale(m.w & 0xFFFFu, p2);
-            s[7] = group_scale(m.w >> 16, p2);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s_scale[threadIdx.x * 8 + i] = s[i];
-            if (geo.col_ok && t.c == 0) {
-                float4* dst = reinterpret_cast<float4*>(scales + (int64_t)t.g * K + geo.col);
-                dst[0] = make_float4(s[0], s[1], s[2], s[3]);
-                dst[1] = make_float4(s[4], s[5], s[6], s[7]);
-            }
-        }
-        __syncthreads();
+        // every lane derives its own 8 scales; lanes of row 0 store them
+        const bool p2 = pow2 != 0;
+        const float s0 = group_scale(m.x & 0xFFFFu, p2), s1 = group_scale(m.x >> 16, p2);
+        const float s2 = group_scale(m.y & 0xFFFFu, p2), s3 = group_scale(m.y >> 16, p2);
+        const float s4 = group_scale(m.z & 0xFFFFu, p2), s5 = group_scale(m.z >> 16, p2);
+        const float s6 = group_scale(m.w & 0xFFFFu, p2), s7 = group_scale(m.w >> 16, p2);
         if (geo.col_ok) {
-            const float* ss = s_scale + geo.tx * 8;
-            const float s0 = ss[0], s1 = ss[1], s2 = ss[2], s3 = ss[3];
-            const float s4 = ss[4], s5 = ss[5], s6 = ss[6], s7 = ss[7];
+            if (geo.ty == 0 && t.c == 0) {
+                float4* dst = reinterpret_cast<float4*>(scales + (int64_t)t.g * K + geo.col);
+                dst[0] = make_float4(s0, s1, s2, s3);
+                dst[1] = make_float4(s4, s5, s6, s7);
+            }
 #pragma unroll
             for (int s = 0; s < kSlabs; ++s) {
                 if (s * geo.rps < nrows) {
@@ -451,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
                 }
             }
         }
-        __syncthreads();     // s_scale is reused by the next item
+        __syncthreads();     // red is rewritten by the next item
     }
 }
 
