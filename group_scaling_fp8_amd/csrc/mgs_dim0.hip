@@ -86,7 +86,8 @@ struct GroupInfo {
     int chunks;     // workspace rows (classes T, C)
 };
 
-__device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, int K, int team_max) {
+__device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, int K, int team_max,
+                                                int lt_cap) {
     GroupInfo gi;
     gi.start = start;
     gi.R = end - start;
@@ -101,7 +102,7 @@ __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, 
         gi.cls = kClassA;
     }
     // no strip wider than needed to cover K
-    while (gi.lt > 3 && (8 << (gi.lt - 1)) >= K) --gi.lt;
+    gi.lt = min(gi.lt, lt_cap);
     gi.ns = (K + (8 << gi.lt) - 1) >> (gi.lt + 3);
     gi.chunks = (valid && gi.cls != kClassA) ? gi.nc : 0;
     gi.cnt_x = (valid && gi.cls == kClassC) ? gi.nc * gi.ns : 0;
@@ -134,6 +135,16 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
     t.cls = __builtin_amdgcn_readlane(gi.cls, src);
     t.lt = __builtin_amdgcn_readlane(gi.lt, src);
     t.nc = nc;
+    t.g0 = start;
+    t.g1 = start + R;
+    if (t.cls == kClassA) {          // one tile per strip: no division
+        t.c = 0;
+        t.strip = local;
+        t.r0 = t.g0;
+        t.r1 = t.g1;
+        t.cbase = 0;
+        return;
+    }
     if (t.cls == kClassT) {          // the chunks of a strip together
         t.strip = local / nc;
         t.c = local - t.strip * nc;
@@ -141,23 +152,16 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
         t.c = local / ns;
         t.strip = local - t.c * ns;
     }
-    t.g0 = start;
-    t.g1 = start + R;
-    if (t.cls != kClassA) {
-        const int cs = (R + nc - 1) / nc;
-        t.r0 = min(start + t.c * cs, t.g1);
-        t.r1 = min(start + (t.c + 1) * cs, t.g1);
-    } else {
-        t.r0 = t.g0;
-        t.r1 = t.g1;
-    }
+    const int cs = (R + nc - 1) / nc;
+    t.r0 = min(start + t.c * cs, t.g1);
+    t.r1 = min(start + (t.c + 1) * cs, t.g1);
     t.cbase = __builtin_amdgcn_readlane(chunk_incl, src) - __builtin_amdgcn_readlane(gi.chunks, src);
 }
 
 // Tile number `target` of the order described at the top of this file. Run
 // by every wave of the workgroup; all lanes return the same tile.
 __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
-                          int target) {
+                          int lt_cap, bool maybe_c, int target) {
     const int lane = threadIdx.x & (kWave - 1);
     Tile t;
     t.g = -1;
@@ -168,13 +172,14 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         const int g = base + lane;
         const int raw = min(max(g < G ? off[g] : M, 0), M);
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
-        int start = __shfl_up(end, 1, kWave);
-        if (lane == 0) start = carry_end;
-        const GroupInfo gi = group_info(start, end, g < G, K, team_max);
-        const int incl_x = wave_prefix_sum_dpp(gi.cnt_x) + carry_x;
+        // the previous lane's end (wave_shr:1); lane 0 keeps carry_end
+        const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
+        const GroupInfo gi = group_info(start, end, g < G, K, team_max, lt_cap);
+        const int incl_x = maybe_c ? wave_prefix_sum_dpp(gi.cnt_x) + carry_x : 0;
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
-        const uint64_t hx = __ballot(gi.cnt_x > 0 && target >= incl_x - gi.cnt_x && target < incl_x);
+        const uint64_t hx =
+            maybe_c ? __ballot(gi.cnt_x > 0 && target >= incl_x - gi.cnt_x && target < incl_x) : 0ull;
         if (hx) {
             const int src = __ffsll((unsigned long long)hx) - 1;
             const int local = target - (__builtin_amdgcn_readlane(incl_x, src) -
@@ -191,6 +196,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
                 take_tile(t, gi, incl_ch, src, base + src, local, 0);
             }
         }
+        if (t.g >= 0 && !maybe_c) return t;
         carry_end = __builtin_amdgcn_readlane(end, kWave - 1);
         carry_x = __builtin_amdgcn_readlane(incl_x, kWave - 1);
         carry_m = __builtin_amdgcn_readlane(incl_m, kWave - 1);
@@ -206,9 +212,8 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         const int g = base + lane;
         const int raw = min(max(g < G ? off[g] : M, 0), M);
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
-        int start = __shfl_up(end, 1, kWave);
-        if (lane == 0) start = carry_end;
-        const GroupInfo gi = group_info(start, end, g < G, K, team_max);
+        const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
+        const GroupInfo gi = group_info(start, end, g < G, K, team_max, lt_cap);
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
         const uint64_t hm = __ballot(gi.cnt_m > 0 && target >= incl_m - gi.cnt_m && target < incl_m);
@@ -369,13 +374,13 @@ __device__ __forceinline__ bool gather_maxima(uint64_t* ws_max, const Tile& t, i
 __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
-        const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max, uint32_t gen_arg,
-        long long spin_ticks) {
+        int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
+        uint32_t gen_arg, long long spin_ticks) {
     __shared__ uint4 red[kThreads];
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile(off, G, M, K, team_max, (int)item);
+        const Tile t = find_tile(off, G, M, K, team_max, lt_cap, maybe_c, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);
         const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
@@ -469,9 +474,15 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
     char* base = static_cast<char*>(ws);
     const uint32_t* ws_epoch = base ? reinterpret_cast<const uint32_t*>(base + w.epoch_off) : nullptr;
     uint64_t* ws_max = base ? reinterpret_cast<uint64_t*>(base + w.max_off) : nullptr;
+    // strips never wider than K needs: the smallest lt >= 3 with 8 << lt >= K
+    int lt_cap = 3;
+    while (lt_cap < 7 && (int64_t(8) << lt_cap) < K) ++lt_cap;
+    // a group can need column-maximum tiles only if M rows make more chunks
+    // than a team may have
+    const int maybe_c = (int64_t)M > (int64_t)kRowsW128 * team_max ? 1 : 0;
     hipLaunchKernelGGL(dim0_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, M, K, off,
-                       G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max, ws_epoch, ws_max, gen,
-                       spin_ticks);
+                       G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
+                       ws_max, gen, spin_ticks);
     return hipGetLastError();
 }
 
