@@ -9,7 +9,8 @@ fallback: if libmgs.so is missing, the first call raises.
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
-    MGS_ERR_HIP, MGS_ERR_INVALID_ARG, MGS_ERR_UNSUPPORTED, MGS_FLAG_POW2_SCALE, MGS_MAX_GROUPS,
+    MGS_ERR_HIP, MGS_ERR_INVALID_ARG, MGS_ERR_UNSUPPORTED, MGS_FLAG_POW2_SCALE, MGS_FLAG_VALIDATE,
+    MGS_MAX_GROUPS,
     MGS_MX_FLOOR, MGS_MX_RCEIL, MGS_OK, MgsError, lib, library_path,
 )
 from .api import (  # noqa: F401

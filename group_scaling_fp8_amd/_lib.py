@@ -13,6 +13,7 @@ MGS_ERR_INVALID_ARG = 1
 MGS_ERR_UNSUPPORTED = 2
 MGS_ERR_HIP = 3
 MGS_FLAG_POW2_SCALE = 1
+MGS_FLAG_VALIDATE = 2
 MGS_MX_FLOOR = 0
 MGS_MX_RCEIL = 1
 MGS_MAX_GROUPS = 1024

@@ -12,7 +12,7 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import MGS_FLAG_POW2_SCALE, MGS_MX_FLOOR, MGS_MX_RCEIL, check, lib
+from ._lib import MGS_FLAG_POW2_SCALE, MGS_FLAG_VALIDATE, MGS_MX_FLOOR, MGS_MX_RCEIL, check, lib
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
@@ -45,9 +45,14 @@ def _out(t, shape, dtype, device, name):
     return t
 
 
+def _flags(pow2: bool, validate: bool) -> int:
+    # validate: the library copies the offsets to the host and rejects bad ones
+    return (MGS_FLAG_POW2_SCALE if pow2 else 0) | (MGS_FLAG_VALIDATE if validate else 0)
+
+
 def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
                           q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
-                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                          stream=None, validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-group scaling along dim0: x (M, K) bf16, int32 end offsets over M.
     Returns q (M, K) uint8 E4M3 and scales (G, K) float32."""
     _need(x, "x", _BF16_LIKE, 2)
@@ -57,7 +62,7 @@ def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = F
     q = _out(q, (M, K), torch.uint8, x.device, "q")
     scales = _out(scales, (G, K), torch.float32, x.device, "scales")
     st = lib().mgs_quant_groups_dim0(x.data_ptr(), M, K, offsets.data_ptr(), G,
-                                     MGS_FLAG_POW2_SCALE if pow2 else 0, q.data_ptr(),
+                                     _flags(pow2, validate), q.data_ptr(),
                                      scales.data_ptr(), _stream_handle(stream))
     check("mgs_quant_groups_dim0", st)
     return q, scales
@@ -65,7 +70,7 @@ def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = F
 
 def mgs_quant_groups_dim1(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
                           q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
-                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                          stream=None, validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-group rowwise scaling: x (M, K) bf16, int32 end offsets over K
     (multiples of 16). Returns q (M, K) uint8 E4M3 and scales (M, G) float32."""
     _need(x, "x", _BF16_LIKE, 2)
@@ -75,7 +80,7 @@ def mgs_quant_groups_dim1(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = F
     q = _out(q, (M, K), torch.uint8, x.device, "q")
     scales = _out(scales, (M, G), torch.float32, x.device, "scales")
     st = lib().mgs_quant_groups_dim1(x.data_ptr(), M, K, offsets.data_ptr(), G,
-                                     MGS_FLAG_POW2_SCALE if pow2 else 0, q.data_ptr(),
+                                     _flags(pow2, validate), q.data_ptr(),
                                      scales.data_ptr(), _stream_handle(stream))
     check("mgs_quant_groups_dim1", st)
     return q, scales

@@ -7,6 +7,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "mgs.h"
 #include "mgs_kernels.hpp"
@@ -86,12 +87,35 @@ hipError_t dim0_workspace_for(hipStream_t stream, const mgs::Dim0Workspace& layo
     return hipSuccess;
 }
 
+// MGS_FLAG_VALIDATE: the offsets, copied to the host in stream order, must be
+// non-decreasing multiples of `align` in [0, extent] ending at extent.
+int validate_offsets(const int32_t* offsets, int32_t n_groups, int64_t extent, int align,
+                     hipStream_t stream) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_status(e);
+    if (cap != hipStreamCaptureStatusNone) return MGS_ERR_UNSUPPORTED;
+    std::vector<int32_t> h((size_t)n_groups);
+    e = hipMemcpyAsync(h.data(), offsets, (size_t)n_groups * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+    int64_t prev = 0;
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const int64_t v = h[(size_t)g];
+        if (v < prev || v > extent || v % align != 0) return MGS_ERR_INVALID_ARG;
+        prev = v;
+    }
+    return prev == extent ? MGS_OK : MGS_ERR_INVALID_ARG;
+}
+
 int check_grouped(const void* x, int64_t M, int64_t K, const int32_t* offsets, int32_t n_groups,
                   uint32_t flags, const void* q, const float* scales) {
     if (M < 0 || K < 0) return MGS_ERR_INVALID_ARG;
     if (n_groups < 1) return MGS_ERR_INVALID_ARG;
     if (n_groups > MGS_MAX_GROUPS) return MGS_ERR_UNSUPPORTED;
-    if (flags & ~MGS_FLAG_POW2_SCALE) return MGS_ERR_INVALID_ARG;
+    if (flags & ~(MGS_FLAG_POW2_SCALE | MGS_FLAG_VALIDATE)) return MGS_ERR_INVALID_ARG;
     if (!offsets || !aligned(offsets, 4)) return MGS_ERR_INVALID_ARG;
     if (M > INT32_MAX || K > INT32_MAX) return MGS_ERR_UNSUPPORTED;  // offsets are int32
     if (M * K > 0) {
@@ -160,6 +184,10 @@ int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* of
     if (K % 8 != 0) return MGS_ERR_INVALID_ARG;
     if (K == 0) return MGS_OK;
     if (!scales || !aligned(scales, 16)) return MGS_ERR_INVALID_ARG;
+    if (flags & MGS_FLAG_VALIDATE) {
+        st = validate_offsets(offsets, n_groups, M, 1, reinterpret_cast<hipStream_t>(stream));
+        if (st != MGS_OK) return st;
+    }
     const mgs::DeviceInfo dinfo = mgs::device_info();
     const int team_max = mgs::dim0_team_max(dinfo);
     if (mgs::dim0_tile_bound(M, K, n_groups, team_max) >= INT32_MAX) return MGS_ERR_UNSUPPORTED;
@@ -195,6 +223,10 @@ int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* of
     if (K > MGS_DIM1_MAX_K) return MGS_ERR_UNSUPPORTED;
     if (M == 0 || K == 0) return MGS_OK;
     if (!scales || !aligned(scales, 4)) return MGS_ERR_INVALID_ARG;
+    if (flags & MGS_FLAG_VALIDATE) {
+        st = validate_offsets(offsets, n_groups, K, 16, reinterpret_cast<hipStream_t>(stream));
+        if (st != MGS_OK) return st;
+    }
     return hip_status(mgs::launch_dim1(static_cast<const uint16_t*>(x), M, (int)K, offsets,
                                        n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
                                        static_cast<uint8_t*>(q), scales,

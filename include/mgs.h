@@ -54,6 +54,13 @@ typedef enum {
 } mgs_status;
 
 #define MGS_FLAG_POW2_SCALE 1u /* round scales down to a power of two */
+/* Debug aid for the two grouped entry points: copy the offsets to the host
+ * (synchronising the stream) and return MGS_ERR_INVALID_ARG unless they are
+ * non-decreasing, within [0, extent], end at the extent (M for dim0, K for
+ * dim1) and, for dim1, are multiples of 16. Without it, device offsets are
+ * not checked (bad ones give unspecified values, never an out-of-bounds
+ * access). MGS_ERR_UNSUPPORTED on a stream that is capturing a graph. */
+#define MGS_FLAG_VALIDATE 2u
 
 enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
 

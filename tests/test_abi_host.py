@@ -58,7 +58,8 @@ def test_grouped_argument_errors(L, fn):
     assert call(G=0) == INVALID
     assert call(G=-3) == INVALID
     assert call(G=mgs.MGS_MAX_GROUPS + 1) == UNSUPPORTED
-    assert call(flags=2) == INVALID
+    assert call(flags=4) == INVALID
+    assert call(flags=0x80000000) == INVALID
     assert call(off=None) == INVALID
     assert call(off=A + 2) == INVALID
     assert call(x=None) == INVALID

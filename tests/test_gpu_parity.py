@@ -324,3 +324,30 @@ def test_bad_offsets_stay_in_bounds():
         o = np.array(off, np.int32)
         gpu_dim0(x, o)
         gpu_dim1(x, o)
+
+
+def test_validate_flag():
+    """MGS_FLAG_VALIDATE: good offsets give the oracle's bytes; malformed
+    ones are rejected with MGS_ERR_INVALID_ARG before any launch."""
+    rng = np.random.default_rng(11)
+    x = wl.randn_bf16(rng, (200, 64), 1.0)
+    xt = to_dev(x)
+    good = np.array([48, 48, 200], np.int32)
+    q, s = mgs.mgs_quant_groups_dim0(xt, to_dev(good), validate=True)
+    rq, rs = oracle.quant_groups_dim0(x, good)
+    assert_same_bytes(q.cpu().numpy(), rq, "dim0 q (validated)")
+    assert_same_bytes(s.cpu().numpy(), rs, "dim0 scales (validated)")
+    good1 = np.array([16, 16, 64], np.int32)
+    q1, s1 = mgs.mgs_quant_groups_dim1(xt, to_dev(good1), validate=True)
+    rq1, rs1 = oracle.quant_groups_dim1(x, good1)
+    assert_same_bytes(q1.cpu().numpy(), rq1, "dim1 q (validated)")
+    assert_same_bytes(s1.cpu().numpy(), rs1, "dim1 scales (validated)")
+    bad_dim0 = ([100, 50, 200], [100, 300], [100, 150], [-1, 200])
+    for off in bad_dim0:
+        with pytest.raises(mgs.MgsError) as e:
+            mgs.mgs_quant_groups_dim0(xt, to_dev(np.array(off, np.int32)), validate=True)
+        assert e.value.status == mgs.MGS_ERR_INVALID_ARG, off
+    for off in ([8, 64], [32, 16, 64], [16, 48], [16, 80]):
+        with pytest.raises(mgs.MgsError) as e:
+            mgs.mgs_quant_groups_dim1(xt, to_dev(np.array(off, np.int32)), validate=True)
+        assert e.value.status == mgs.MGS_ERR_INVALID_ARG, off
