@@ -268,6 +268,7 @@ def main():
 
 # kernel-name fragments of the library's kernels, and what each one is
 KERNELS = (("copy_kernel", "copy"), ("dim0_kernel", "dim0_kernel"),
+           ("dim0t_kernel", "dim0t_kernel"),
            ("dim0_epoch_bump_kernel", "dim0_epoch_bump_kernel"),
            ("dim1_kernel", "dim1_kernel"), ("mx_kernel", "mx_kernel"))
 COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
@@ -339,7 +340,8 @@ def counter_run(torch, mgs, wl, dev, reps):
     the cache-evicting read between launches, so a counter collector sees
     one dispatch per launch: the 256 MiB copy kernel (known traffic,
     268435456 B read + written), dim0 on T (16640, 8192) G=64, dim1 on T^T
-    G=64, the MX cast on (131072, 5120) FLOOR and RCEIL."""
+    G=64, the MX cast on (131072, 5120) FLOOR and RCEIL, and the transposed
+    dim0 on T G=64."""
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -354,11 +356,13 @@ def counter_run(torch, mgs, wl, dev, reps):
     q0, s0 = mgs.mgs_quant_groups_dim0(x0, off)
     q1, s1 = mgs.mgs_quant_groups_dim1(x1, off)
     q5, s5 = mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR)
+    qt, st = mgs.mgs_quant_groups_dim0_t(x0, off)
     runs = [lambda: mgs.mgs_copy(src, dst),
             lambda: mgs.mgs_quant_groups_dim0(x0, off, q=q0, scales=s0),
             lambda: mgs.mgs_quant_groups_dim1(x1, off, q=q1, scales=s1),
             lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR, q=q5, scales=s5),
-            lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q5, scales=s5)]
+            lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q5, scales=s5),
+            lambda: mgs.mgs_quant_groups_dim0_t(x0, off, q_t=qt, scales_t=st)]
     for fn in runs:
         for _ in range(reps):
             flush.max()
@@ -436,6 +440,15 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
                                                   wl.c4_dim1(64, T)]:
         add(w.name, w.kind, w.x, w.offsets, w.algorithmic_bytes(), grouped(w))
         del w
+    # the fused quantize + transpose of T: (8192, 16640) e4m3 and (8192, 64)
+    # scales, the same bytes as dim0 at this shape
+    w = wl.c6_dim0_target(64, T)
+    xt6 = torch.from_numpy(T.view(np.int16)).to(dev)
+    ot6 = torch.from_numpy(w.offsets).to(dev)
+    qt6, st6 = mgs.mgs_quant_groups_dim0_t(xt6, ot6)
+    add("dim0_t (16640,8192) G=64 -> (8192,16640)", "dim0_t", T, w.offsets, w.algorithmic_bytes(),
+        lambda: (lambda: mgs.mgs_quant_groups_dim0_t(xt6, ot6, q_t=qt6, scales_t=st6)))
+    del w, xt6, ot6, qt6, st6
     c5 = wl.c5_mx()
     x5 = torch.from_numpy(c5.x.view(np.int16)).to(dev)
     for mode, nm in ((mgs.MGS_MX_FLOOR, "FLOOR"), (mgs.MGS_MX_RCEIL, "RCEIL")):

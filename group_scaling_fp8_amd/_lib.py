@@ -20,7 +20,8 @@ MGS_MAX_GROUPS = 1024
 MGS_DIM1_MAX_K = 131072
 
 EXPORTS = (
-    "mgs_quant_groups_dim0", "mgs_quant_groups_dim1", "mgs_mx_quant_dim0", "mgs_cast_e4m3",
+    "mgs_quant_groups_dim0", "mgs_quant_groups_dim0_t", "mgs_quant_groups_dim1", "mgs_mx_quant_dim0",
+    "mgs_cast_e4m3",
     "mgs_copy", "mgs_status_string", "mgs_last_hip_error",
 )
 
@@ -52,7 +53,7 @@ def lib():
                 "g.build()'` or `python group_scaling_fp8_amd/build.py`" % _LIB_PATH)
         L = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
-        for name in ("mgs_quant_groups_dim0", "mgs_quant_groups_dim1"):
+        for name in ("mgs_quant_groups_dim0", "mgs_quant_groups_dim0_t", "mgs_quant_groups_dim1"):
             fn = getattr(L, name)
             fn.argtypes = [vp, i64, i64, vp, i32, u32, vp, vp, vp]
             fn.restype = ctypes.c_int

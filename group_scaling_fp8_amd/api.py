@@ -68,6 +68,26 @@ def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = F
     return q, scales
 
 
+def mgs_quant_groups_dim0_t(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
+                            q_t: Optional[torch.Tensor] = None,
+                            scales_t: Optional[torch.Tensor] = None, stream=None,
+                            validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-group scaling along dim0 with transposed outputs: x (M, K) bf16,
+    int32 end offsets over M (multiples of 16). Returns q_t (K, M) uint8
+    E4M3 and scales_t (K, G) float32, the transposes of dim0's outputs."""
+    _need(x, "x", _BF16_LIKE, 2)
+    _need(offsets, "offsets", (torch.int32,), 1)
+    M, K = x.shape
+    G = offsets.shape[0]
+    q_t = _out(q_t, (K, M), torch.uint8, x.device, "q_t")
+    scales_t = _out(scales_t, (K, G), torch.float32, x.device, "scales_t")
+    st = lib().mgs_quant_groups_dim0_t(x.data_ptr(), M, K, offsets.data_ptr(), G,
+                                       _flags(pow2, validate), q_t.data_ptr(),
+                                       scales_t.data_ptr(), _stream_handle(stream))
+    check("mgs_quant_groups_dim0_t", st)
+    return q_t, scales_t
+
+
 def mgs_quant_groups_dim1(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
                           q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
                           stream=None, validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:

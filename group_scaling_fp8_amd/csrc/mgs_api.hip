@@ -172,25 +172,25 @@ int dim0_team_max(const DeviceInfo& d) {
     return d.team_max;
 }
 
-}  // namespace mgs
-
-extern "C" {
-
-int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
-                          int32_t n_groups, uint32_t flags, void* q, float* scales,
-                          void* stream) {
+// Both dim0 entry points: q (M, K) and scales (G, K), or their transposes.
+int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                      int32_t n_groups, uint32_t flags, void* q, float* scales, void* stream,
+                      bool transposed) {
     int st = check_grouped(x, M, K, offsets, n_groups, flags, q, scales);
     if (st != MGS_OK) return st;
     if (K % 8 != 0) return MGS_ERR_INVALID_ARG;
+    if (transposed && (M % 16 != 0 || (M * K > 0 && !aligned(q, 16)))) return MGS_ERR_INVALID_ARG;
     if (K == 0) return MGS_OK;
-    if (!scales || !aligned(scales, 16)) return MGS_ERR_INVALID_ARG;
+    if (!scales || !aligned(scales, transposed ? 4 : 16)) return MGS_ERR_INVALID_ARG;
     if (flags & MGS_FLAG_VALIDATE) {
-        st = validate_offsets(offsets, n_groups, M, 1, reinterpret_cast<hipStream_t>(stream));
+        st = validate_offsets(offsets, n_groups, M, transposed ? 16 : 1,
+                              reinterpret_cast<hipStream_t>(stream));
         if (st != MGS_OK) return st;
     }
     const mgs::DeviceInfo dinfo = mgs::device_info();
     const int team_max = mgs::dim0_team_max(dinfo);
-    if (mgs::dim0_tile_bound(M, K, n_groups, team_max) >= INT32_MAX) return MGS_ERR_UNSUPPORTED;
+    if (mgs::dim0_tile_bound(M, K, n_groups, team_max) >= INT32_MAX)
+        return MGS_ERR_UNSUPPORTED;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);
     void* ws = nullptr;
@@ -209,9 +209,25 @@ int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* of
         }
     }
     return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, (int)K, offsets,
-                                       n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
+                                       n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0, transposed,
                                        static_cast<uint8_t*>(q), scales, team_max, ws, gen,
                                        mgs::dim0_spin_ticks(dinfo), s));
+}
+
+}  // namespace mgs
+
+extern "C" {
+
+int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                          int32_t n_groups, uint32_t flags, void* q, float* scales,
+                          void* stream) {
+    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q, scales, stream, false);
+}
+
+int mgs_quant_groups_dim0_t(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                            int32_t n_groups, uint32_t flags, void* q_t, float* scales_t,
+                            void* stream) {
+    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q_t, scales_t, stream, true);
 }
 
 int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* offsets,

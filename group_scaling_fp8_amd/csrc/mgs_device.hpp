@@ -56,6 +56,16 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// 16 bytes of output written once, with a nontemporal store.
+__device__ __forceinline__ void store_stream16(void* p, uint4 v) {
+    u32x4 t;
+    t.x = v.x;
+    t.y = v.y;
+    t.z = v.z;
+    t.w = v.w;
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+}
+
 // 8 bytes of output written once, with a nontemporal store.
 __device__ __forceinline__ void store_stream(void* p, uint2 v) {
     u32x2 t;

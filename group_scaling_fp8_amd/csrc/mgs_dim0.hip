@@ -125,7 +125,7 @@ __device__ __forceinline__ int wave_prefix_sum_dpp(int v) {
 // Fills t from lane src's group, tile `local` inside that group. src is
 // wave-uniform, so the fields land in scalar registers.
 __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chunk_incl, int src,
-                                          int g, int local, int maxima) {
+                                          int g, int local, int maxima, int row_align) {
     const int ns = __builtin_amdgcn_readlane(gi.ns, src);
     const int nc = __builtin_amdgcn_readlane(gi.nc, src);
     const int start = __builtin_amdgcn_readlane(gi.start, src);
@@ -152,7 +152,8 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
         t.c = local / ns;
         t.strip = local - t.c * ns;
     }
-    const int cs = (R + nc - 1) / nc;
+    // chunk rows, rounded up to row_align (a power of two; at most 640 still)
+    const int cs = ((R + nc - 1) / nc + row_align - 1) & -row_align;
     t.r0 = min(start + t.c * cs, t.g1);
     t.r1 = min(start + (t.c + 1) * cs, t.g1);
     t.cbase = __builtin_amdgcn_readlane(chunk_incl, src) - __builtin_amdgcn_readlane(gi.chunks, src);
@@ -161,7 +162,7 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
 // Tile number `target` of the order described at the top of this file. Run
 // by every wave of the workgroup; all lanes return the same tile.
 __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
-                          int lt_cap, bool maybe_c, int target) {
+                          int lt_cap, bool maybe_c, int row_align, int target) {
     const int lane = threadIdx.x & (kWave - 1);
     Tile t;
     t.g = -1;
@@ -170,7 +171,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
     int carry_end = 0, carry_x = 0, carry_m = 0, carry_ch = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
-        const int raw = min(max(g < G ? off[g] : M, 0), M);
+        const int raw = min(max(g < G ? off[g] : M, 0), M) & -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         // the previous lane's end (wave_shr:1); lane 0 keeps carry_end
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
@@ -184,7 +185,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
             const int src = __ffsll((unsigned long long)hx) - 1;
             const int local = target - (__builtin_amdgcn_readlane(incl_x, src) -
                                         __builtin_amdgcn_readlane(gi.cnt_x, src));
-            take_tile(t, gi, incl_ch, src, base + src, local, 1);
+            take_tile(t, gi, incl_ch, src, base + src, local, 1, row_align);
             return t;
         }
         if (t.g < 0) {
@@ -193,7 +194,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
                 const int src = __ffsll((unsigned long long)hm) - 1;
                 const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
                                             __builtin_amdgcn_readlane(gi.cnt_m, src));
-                take_tile(t, gi, incl_ch, src, base + src, local, 0);
+                take_tile(t, gi, incl_ch, src, base + src, local, 0, row_align);
             }
         }
         if (t.g >= 0 && !maybe_c) return t;
@@ -210,7 +211,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
     carry_end = carry_m = carry_ch = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
-        const int raw = min(max(g < G ? off[g] : M, 0), M);
+        const int raw = min(max(g < G ? off[g] : M, 0), M) & -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
         const GroupInfo gi = group_info(start, end, g < G, K, team_max, lt_cap);
@@ -221,7 +222,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
             const int src = __ffsll((unsigned long long)hm) - 1;
             const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
                                         __builtin_amdgcn_readlane(gi.cnt_m, src));
-            take_tile(t, gi, incl_ch, src, base + src, local, 0);
+            take_tile(t, gi, incl_ch, src, base + src, local, 0, row_align);
             return t;
         }
         carry_end = __builtin_amdgcn_readlane(end, kWave - 1);
@@ -282,14 +283,24 @@ __device__ __forceinline__ TileGeom tile_geom(const Tile& t, int K) {
     return q;
 }
 
+// Tile row held in vector s by a lane of row index ty. Plain layout: rows
+// s * rps + ty. Quad layout (transposed output): vectors 4j .. 4j + 3 hold
+// four consecutive rows 4 * (j * rps + ty) + 0..3, so that a lane can turn
+// them into 4-byte column words.
+template <bool kQuad>
+__device__ __forceinline__ int slab_row(int s, int rps, int ty) {
+    return kQuad ? 4 * ((s >> 2) * rps + ty) + (s & 3) : s * rps + ty;
+}
+
 // Loads rows [r0, r0 + nrows) of this lane's 8 columns into registers.
+template <bool kQuad>
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t K, int r0, int nrows,
                                           const TileGeom& q, uint4 (&v)[kSlabs]) {
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
         v[s] = make_uint4(0u, 0u, 0u, 0u);
-        if (s * q.rps < nrows) {
-            const int rr = s * q.rps + q.ty;
+        if (slab_row<kQuad>(s, q.rps, 0) < nrows) {
+            const int rr = slab_row<kQuad>(s, q.rps, q.ty);
             if (rr < nrows && q.col_ok) v[s] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
         }
     }
@@ -367,20 +378,48 @@ __device__ __forceinline__ bool gather_maxima(uint64_t* ws_max, const Tile& t, i
     return true;
 }
 
-}  // namespace
+// Byte transpose of a 4 x 4 block: a, b, c, d hold bytes 0..3 of four
+// consecutive rows; word j of out holds byte j of a, b, c, d (low to high).
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                             uint32_t (&out)[4]) {
+    // v_perm_b32 picks bytes of {hi, lo}: selector bytes 0..3 address lo,
+    // 4..7 address hi
+    const uint32_t ab01 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+    const uint32_t ab23 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+    const uint32_t cd01 = __builtin_amdgcn_perm(d, c, 0x05010400u);
+    const uint32_t cd23 = __builtin_amdgcn_perm(d, c, 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(cd01, ab01, 0x05040100u);           // a0 b0 c0 d0
+    out[1] = __builtin_amdgcn_perm(cd01, ab01, 0x07060302u);           // a1 b1 c1 d1
+    out[2] = __builtin_amdgcn_perm(cd23, ab23, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(cd23, ab23, 0x07060302u);
+}
 
-// ws layout (Dim0Workspace): the epoch word, then maxima[chunk][K / 2]
-// 64-bit words (generation << 32 | two 16-bit magnitude patterns).
-__global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
+// Staging of the transposed tile in LDS: per tile column a row of 4-byte
+// words (a multiple of 16 of them), each word holding four consecutive rows.
+// The word index is XOR-swizzled with the lane's column block (within its
+// 16-word block) so that the lanes of a wave spread over the banks. Three
+// quads of rows of any strip width fit: 8 << lt columns x 16 * 2^(7 - lt)
+// words at most 16384 words.
+constexpr int kStageWords = 16384;        // 64 KiB
+__device__ __forceinline__ int stage_pitch(int rps) {
+    return (3 * rps + 15) & ~15;          // words per column: three quads of rows
+}
+__device__ __forceinline__ int stage_swizzle(int col_block) { return (col_block & 3) << 2; }
+
+// One tile: load, column amax (across chunk tiles when the group is cut),
+// scales, cast. kT: q is (K, M) and scales (K, G), the transposes of dim0's
+// outputs, written through the LDS stage.
+template <bool kT>
+__device__ __forceinline__ void dim0_body(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks) {
-    __shared__ uint4 red[kThreads];
+        uint32_t gen_arg, long long spin_ticks, uint4* red, uint32_t* stage) {
+    constexpr int kRowAlign = kT ? 16 : 1;
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile(off, G, M, K, team_max, lt_cap, maybe_c, (int)item);
+        const Tile t = find_tile(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);
         const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
@@ -399,11 +438,11 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         }
 
         uint4 v[kSlabs];
-        load_tile(x, K, t.r0, nrows, geo, v);
+        load_tile<kT>(x, K, t.r0, nrows, geo, v);
         if (t.cls != kClassC || t.maxima) {
 #pragma unroll
             for (int s = 0; s < kSlabs; ++s)
-                if (s * geo.rps < nrows) max4(m, v[s]);
+                if (slab_row<kT>(s, geo.rps, 0) < nrows) max4(m, v[s]);
         }
 
         if (t.maxima) {
@@ -434,24 +473,116 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const float s2 = group_scale(m.y & 0xFFFFu, p2), s3 = group_scale(m.y >> 16, p2);
         const float s4 = group_scale(m.z & 0xFFFFu, p2), s5 = group_scale(m.z >> 16, p2);
         const float s6 = group_scale(m.w & 0xFFFFu, p2), s7 = group_scale(m.w >> 16, p2);
-        if (geo.col_ok) {
-            if (geo.ty == 0 && t.c == 0) {
-                float4* dst = reinterpret_cast<float4*>(scales + (int64_t)t.g * K + geo.col);
-                dst[0] = make_float4(s0, s1, s2, s3);
-                dst[1] = make_float4(s4, s5, s6, s7);
-            }
+        if (!kT) {
+            if (geo.col_ok) {
+                if (geo.ty == 0 && t.c == 0) {
+                    float4* dst = reinterpret_cast<float4*>(scales + (int64_t)t.g * K + geo.col);
+                    dst[0] = make_float4(s0, s1, s2, s3);
+                    dst[1] = make_float4(s4, s5, s6, s7);
+                }
 #pragma unroll
-            for (int s = 0; s < kSlabs; ++s) {
-                if (s * geo.rps < nrows) {
-                    const int rr = s * geo.rps + geo.ty;
-                    if (rr < nrows)
-                        store_stream(q + (int64_t)(t.r0 + rr) * K + geo.col,
-                                     cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
+                for (int s = 0; s < kSlabs; ++s) {
+                    if (s * geo.rps < nrows) {
+                        const int rr = s * geo.rps + geo.ty;
+                        if (rr < nrows)
+                            store_stream(q + (int64_t)(t.r0 + rr) * K + geo.col,
+                                         cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
+                    }
+                }
+            }
+        } else {
+            if (geo.col_ok && geo.ty == 0 && t.c == 0) {
+                float* dst = scales + (int64_t)geo.col * G + t.g;
+                dst[0] = s0;
+                dst[(int64_t)G] = s1;
+                dst[2 * (int64_t)G] = s2;
+                dst[3 * (int64_t)G] = s3;
+                dst[4 * (int64_t)G] = s4;
+                dst[5 * (int64_t)G] = s5;
+                dst[6 * (int64_t)G] = s6;
+                dst[7 * (int64_t)G] = s7;
+            }
+            // Two phases through the stage: row quads 0..2, then 3..4. Tile
+            // rows and their starts are multiples of 16, so every quad is
+            // whole and every output piece is 16 aligned bytes.
+            const int pw = stage_pitch(geo.rps);
+            const int W = geo.tpr * 8;
+            const int ncols = min(W, K - t.strip * W);
+            for (int ph = 0; ph < 2; ++ph) {
+                const int qa = ph ? 3 : 0, qb = ph ? 5 : 3;
+                const int row_a = 4 * qa * geo.rps;
+                if (row_a >= nrows) break;
+                const int row_b = min(4 * qb * geo.rps, nrows);
+                if (ph) __syncthreads();      // the stage's first-phase reads are done
+                uint32_t* col_base = stage + geo.tx * 8 * pw;
+#pragma unroll
+                for (int qd = 0; qd < kSlabs / 4; ++qd) {
+                    if ((qd >= 3) != (ph == 1)) continue;
+                    const int row = 4 * (qd * geo.rps + geo.ty);
+                    if (row < nrows && geo.col_ok) {
+                        const uint2 b0 = cast8(v[4 * qd + 0], s0, s1, s2, s3, s4, s5, s6, s7);
+                        const uint2 b1 = cast8(v[4 * qd + 1], s0, s1, s2, s3, s4, s5, s6, s7);
+                        const uint2 b2 = cast8(v[4 * qd + 2], s0, s1, s2, s3, s4, s5, s6, s7);
+                        const uint2 b3 = cast8(v[4 * qd + 3], s0, s1, s2, s3, s4, s5, s6, s7);
+                        uint32_t lo[4], hi[4];
+                        transpose4x4(b0.x, b1.x, b2.x, b3.x, lo);
+                        transpose4x4(b0.y, b1.y, b2.y, b3.y, hi);
+                        const int w = ((qd - qa) * geo.rps + geo.ty) ^ stage_swizzle(geo.tx);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            col_base[j * pw + w] = lo[j];
+                            col_base[(j + 4) * pw + w] = hi[j];
+                        }
+                    }
+                }
+                __syncthreads();
+                // pieces of 16 rows of one column, consecutive lanes along the
+                // rows of a column: c = p / npc by a multiply-shift, exact since
+                // p < ncols * npc <= 3072 and npc <= 48
+                const int npc = (row_b - row_a) >> 4;
+                const uint32_t inv = ((1u << 20) + (uint32_t)npc - 1u) / (uint32_t)npc;
+                const int total = ncols * npc;
+                uint8_t* qbase = q + (int64_t)(t.strip * W) * M + (t.r0 + row_a);
+                for (int p = threadIdx.x; p < total; p += kThreads) {
+                    const int c = (int)(((uint32_t)p * inv) >> 20);
+                    const int k = p - c * npc;
+                    const uint4 val = *reinterpret_cast<const uint4*>(
+                        stage + c * pw + ((4 * k) ^ stage_swizzle(c >> 3)));
+                    // an ordinary store: a group's run of a q_t row starts on a
+                    // 16-byte boundary only, and L2 merges the two tiles' parts
+                    // of a shared line (nontemporal partial lines cost far more)
+                    *reinterpret_cast<uint4*>(qbase + (int64_t)c * M + 16 * k) = val;
                 }
             }
         }
-        __syncthreads();     // red is rewritten by the next item
+        __syncthreads();     // red (and the stage) are rewritten by the next item
     }
+}
+
+}  // namespace
+
+// ws layout (Dim0Workspace): the epoch word, then maxima[chunk][K / 2]
+// 64-bit words (generation << 32 | two 16-bit magnitude patterns).
+__global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
+        const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
+        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
+        int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
+        uint32_t gen_arg, long long spin_ticks) {
+    __shared__ uint4 red[kThreads];
+    dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
+                     ws_max, gen_arg, spin_ticks, red, nullptr);
+}
+
+// The same per-group scaling with transposed outputs: qT (K, M), scalesT (K, G).
+__global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
+        const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
+        int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
+        int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
+        uint32_t gen_arg, long long spin_ticks) {
+    __shared__ uint4 red[kThreads];
+    __shared__ uint4 stage[kStageWords / 4];
+    dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
+                    ws_max, gen_arg, spin_ticks, red, reinterpret_cast<uint32_t*>(stage));
 }
 
 // Advances the epoch word by one, keeping its top bit set so that epochs
@@ -465,8 +596,8 @@ __global__ void dim0_epoch_bump_kernel(uint32_t* __restrict__ ws_epoch) {
 }
 
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, bool pow2,
-                       uint8_t* q, float* scales, int team_max, void* ws, uint32_t gen,
-                       long long spin_ticks, hipStream_t stream) {
+                       bool transposed, uint8_t* q, float* scales, int team_max, void* ws,
+                       uint32_t gen, long long spin_ticks, hipStream_t stream) {
     const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
     const int64_t grid = n_tiles < kDim0MaxGrid ? n_tiles : kDim0MaxGrid;
@@ -480,9 +611,9 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
     // a group can need column-maximum tiles only if M rows make more chunks
     // than a team may have
     const int maybe_c = (int64_t)M > (int64_t)kRowsW128 * team_max ? 1 : 0;
-    hipLaunchKernelGGL(dim0_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, M, K, off,
-                       G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
-                       ws_max, gen, spin_ticks);
+    hipLaunchKernelGGL(transposed ? dim0t_kernel : dim0_kernel, dim3((unsigned)grid), dim3(kThreads),
+                       0, stream, x, M, K, off, G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max,
+                       lt_cap, maybe_c, ws_epoch, ws_max, gen, spin_ticks);
     return hipGetLastError();
 }
 

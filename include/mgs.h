@@ -108,6 +108,34 @@ int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
                           void *stream);
 
 /*
+ * Per-group scaling along dim0 with transposed outputs ([ROWWISE] Summary:
+ * per-group colwise scales computed on one layout give the per-group rowwise
+ * scales of its transpose; its stacked change names the transpose method as
+ * the way to keep global accesses coalesced). Same values as
+ * mgs_quant_groups_dim0, written transposed in one pass, so the result is
+ * the rowwise per-group scaling of x^T in GEMM-ready row-major form without
+ * x^T ever being stored.
+ *   x        (M, K) bf16, token-major. Groups split the M rows.
+ *   offsets  n_groups int32 end offsets along M, each a multiple of 16 (the
+ *            token-group alignment of [BLOCKSIZE]'s test source),
+ *            1 <= n_groups <= 1024. Ends are rounded down to a multiple of
+ *            16 on the device, so other offsets give unspecified values but
+ *            no out-of-bounds access.
+ *   flags    0, MGS_FLAG_POW2_SCALE, MGS_FLAG_VALIDATE.
+ *   q_t      (K, M) E4M3 bytes, written: q_t[k, r] = dim0's q[r, k].
+ *   scales_t (K, n_groups) fp32, written: scales_t[k, g] = dim0's
+ *            scales[g, k]; empty groups get the amax = 0 value.
+ * Requirements: M % 16 == 0, K % 8 == 0; x and q_t 16-byte aligned,
+ * scales_t 4-byte aligned. M == 0 writes only the scales; K == 0 is a
+ * no-op. Memory, the bounded wait, graph capture and errors are as for
+ * mgs_quant_groups_dim0 (the same tiles).
+ */
+int mgs_quant_groups_dim0_t(const void *x, int64_t M, int64_t K,
+                            const int32_t *offsets, int32_t n_groups,
+                            uint32_t flags, void *q_t, float *scales_t,
+                            void *stream);
+
+/*
  * Per-group rowwise scaling along dim1 ([ROWWISE] Summary).
  *   x       (M, K) bf16. Groups split the K columns.
  *   offsets n_groups int32 end offsets along K. Every offset must be a

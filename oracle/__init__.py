@@ -148,6 +148,17 @@ def quant_groups_dim0(x_bits: np.ndarray, offsets: np.ndarray, pow2: bool = Fals
     return q, s
 
 
+def quant_groups_dim0_t(x_bits: np.ndarray, offsets: np.ndarray, pow2: bool = False):
+    """dim0 with transposed outputs: x (M, K) bf16 bits, int32 end offsets
+    along M -> (q_t (K, M) u8, scales_t (K, G) f32), the transposes of
+    quant_groups_dim0's results ("test and bench new faster method for per
+    group rowwise scaling", Summary: colwise per-group scales of one layout,
+    transposed, are the rowwise per-group scales of its transpose). The
+    values are dim0's; only the layout changes."""
+    q, s = quant_groups_dim0(x_bits, offsets, pow2)
+    return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
+
+
 def quant_groups_dim1(x_bits: np.ndarray, offsets: np.ndarray, pow2: bool = False):
     """x (M, K) bf16 bits, int32 end offsets along K -> (q (M, K) u8, scales (M, G) f32)."""
     x = _bf16_bits(x_bits)

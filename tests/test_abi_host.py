@@ -44,7 +44,8 @@ def test_status_strings(L):
     assert L.mgs_status_string(99) == b"unknown status"
 
 
-@pytest.mark.parametrize("fn", ["mgs_quant_groups_dim0", "mgs_quant_groups_dim1"])
+@pytest.mark.parametrize("fn", ["mgs_quant_groups_dim0", "mgs_quant_groups_dim0_t",
+                                "mgs_quant_groups_dim1"])
 def test_grouped_argument_errors(L, fn):
     f = getattr(L, fn)
     ok = dict(x=A, M=64, K=128, off=A, G=4, flags=0, q=A, s=A, stream=None)
@@ -72,6 +73,12 @@ def test_grouped_argument_errors(L, fn):
         assert call(K=12) == INVALID
         assert call(s=A + 4) == INVALID
         # 1024 groups of 1024-column strips over K = 2^31 - 8: the tile bound reaches 2^31
+        assert call(K=(1 << 31) - 8, G=1024) == UNSUPPORTED
+    elif fn.endswith("dim0_t"):
+        assert call(K=12) == INVALID
+        assert call(M=24) == INVALID            # M % 16
+        assert call(q=A + 8) == INVALID         # q_t takes 16-byte stores
+        assert call(s=A + 2) == INVALID
         assert call(K=(1 << 31) - 8, G=1024) == UNSUPPORTED
     else:
         assert call(K=24) == INVALID

@@ -1,0 +1,108 @@
+"""GPU parity of the transposed dim0 entry point (mgs_quant_groups_dim0_t):
+q_t (K, M) and scales_t (K, G) against the oracle byte for byte, over every
+strip class (1024- down to 128-column strips, K narrower than a strip,
+ragged last strips), empty groups, chunk teams and column-maximum tiles,
+the path that computes the maxima in the waiting tile itself, pow2 scales,
+the benchmark shape on sampled columns, and offsets that are not multiples
+of 16 (values unspecified, writes in bounds). Every output carries guard
+bands."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import group_scaling_fp8_amd as mgs
+from group_scaling_fp8_amd import workloads as wl
+from gpu_util import Guarded, assert_same_bytes, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mgs.lib()
+
+
+def run_dim0_t(x, off, pow2=False):
+    M, K = x.shape
+    gq, gs = Guarded((K, M), torch.uint8), Guarded((K, len(off)), torch.float32)
+    mgs.mgs_quant_groups_dim0_t(to_dev(x), to_dev(off), pow2, q_t=gq.view, scales_t=gs.view)
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    return gq.numpy(), gs.numpy()
+
+
+def check(x, off, what, pow2=False):
+    q, s = run_dim0_t(x, off, pow2)
+    rq, rs = oracle.quant_groups_dim0_t(x, off, pow2)
+    assert_same_bytes(s, rs, what + " scales_t")
+    assert_same_bytes(q, rq, what + " q_t")
+
+
+def data(seed, M, K):
+    return wl.randn_bf16(np.random.default_rng(seed), (M, K), 0.02, 0.003, 8.0)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("K,sizes", [
+    (264, [16, 48, 0, 80, 160, 256, 320, 336, 640]),   # every strip width up to K, ragged K
+    (520, [656, 16, 1296]),                            # two- and three-chunk teams
+    (8, [32, 0, 704, 16]),                             # one 8-column strip
+    (72, [320, 336, 16]),                              # K narrower than a strip
+    (1032, [208, 400, 96]),
+    (2056, [16, 64, 80, 0, 144, 32]),                  # 1024- and 512-column strips
+])
+def test_dim0_t_classes(K, sizes, pow2):
+    off = np.cumsum(sizes).astype(np.int32)
+    M = int(off[-1])
+    check(data(M + K, M, K), off, "sizes %s K=%d" % (sizes, K), pow2)
+
+
+def test_dim0_t_no_rows_writes_scales():
+    x = np.zeros((0, 64), np.uint16)
+    off = np.zeros(3, np.int32)
+    q, s = run_dim0_t(x, off)
+    rq, rs = oracle.quant_groups_dim0_t(x, off)
+    assert q.shape == (64, 0)
+    assert_same_bytes(s, rs, "scales_t of empty groups")
+
+
+@pytest.mark.parametrize("team_max,spin", [("1", None), (None, "-1")])
+def test_dim0_t_tall_groups_other_paths(team_max, spin, monkeypatch):
+    # column-maximum tiles (team limit 1), then the in-tile fallback (no wait)
+    if team_max:
+        monkeypatch.setenv("MGS_DIM0_TEAM_MAX", team_max)
+    if spin:
+        monkeypatch.setenv("MGS_DIM0_SPIN_TICKS", spin)
+    sizes = [1296, 16, 2000]
+    off = np.cumsum(sizes).astype(np.int32)
+    check(data(5, int(off[-1]), 136), off, "tall groups team_max=%s spin=%s" % (team_max, spin))
+
+
+def test_dim0_t_matches_dim0_at_the_benchmark_shape():
+    """(16640, 8192) G=64, the benchmark's offsets: q_t and scales_t are dim0's
+    outputs transposed (GPU against GPU, every byte), and sampled columns
+    match the oracle."""
+    T = wl.token_major_gradient()
+    off = wl.target_offsets(64)
+    xt, ot = to_dev(T), to_dev(off)
+    q0, s0 = mgs.mgs_quant_groups_dim0(xt, ot)
+    qt, st = mgs.mgs_quant_groups_dim0_t(xt, ot)
+    torch.cuda.synchronize()
+    assert torch.equal(qt, q0.t().contiguous()), "q_t differs from dim0's q transposed"
+    assert torch.equal(st.view(torch.int32), s0.t().contiguous().view(torch.int32))
+    cols = np.random.default_rng(9).choice(T.shape[1], 24, replace=False)
+    rq, rs = oracle.quant_groups_dim0_t(np.ascontiguousarray(T[:, cols]), off)
+    assert_same_bytes(qt[torch.from_numpy(cols).to(qt.device)].cpu().numpy(), rq, "sampled q_t rows")
+    assert_same_bytes(st[torch.from_numpy(cols).to(st.device)].cpu().numpy(), rs, "sampled scales_t rows")
+
+
+def test_dim0_t_unaligned_offsets_stay_in_bounds():
+    """Offsets off the 16-row grid (and unsorted ones) give unspecified values
+    but no write outside the outputs."""
+    x = data(7, 320, 136)
+    for off in ([100, 37, 320], [5, 320], [-3, 400, 320], [320]):
+        run_dim0_t(x, np.array(off, np.int32))

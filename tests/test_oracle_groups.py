@@ -209,6 +209,20 @@ def test_transpose_identity(oracle_mod, pow2):
     assert np.array_equal(s1.view(np.uint32), s0.T.view(np.uint32))
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_dim0_transposed_is_dim1_of_the_transpose(oracle_mod, pow2):
+    """quant_groups_dim0_t reaches dim1's loop on T^T (an independent code
+    path in the oracle) bit for bit, with token-group aligned offsets."""
+    rng = np.random.default_rng(43)
+    x = wl.randn_bf16(rng, (320, 40), 0.02, 0.001, 8.0)
+    off = np.array([16, 16, 160, 320], np.int32)
+    qt, st = oracle_mod.quant_groups_dim0_t(x, off, pow2)
+    q1, s1 = oracle_mod.quant_groups_dim1(np.ascontiguousarray(x.T), off, pow2)
+    assert qt.shape == (40, 320) and st.shape == (40, 4)
+    assert np.array_equal(qt, q1)
+    assert np.array_equal(st.view(np.uint32), s1.view(np.uint32))
+
+
 def test_bad_offsets_rejected(oracle_mod):
     x = np.zeros((32, 16), np.uint16)
     for off in ([16, 8, 32], [16, 31], [33], [-1, 32]):
