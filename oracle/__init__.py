@@ -78,6 +78,10 @@ def _load():
         fn.restype = ctypes.c_int
     lib.oracle_mx_quant_dim0.argtypes = [u16p, i64, i64, ctypes.c_int, u8p, u8p]
     lib.oracle_mx_quant_dim0.restype = ctypes.c_int
+    lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_mx_dequant_dim0.argtypes = [u8p, u8p, i64, i64, u16p]
+    lib.oracle_mx_dequant_dim0.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -187,3 +191,28 @@ def mx_quant_dim0(x_bits: np.ndarray, mode: int):
     if rc != 0:
         raise ValueError("oracle mx: K must be a multiple of 32 and mode 0 or 1")
     return q, s
+
+
+def f64_to_bf16(v: float) -> int:
+    """bf16 bits of v rounded once, to nearest even (overflow to infinity;
+    NaN gives 0x7FC0)."""
+    return int(_load().oracle_f64_to_bf16(float(v)))
+
+
+def mx_dequant_dim0(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """q (M, K) E4M3 bytes, scales (M, K/32) E8M0 bytes -> y (M, K) bf16 bits,
+    y = bf16(E4M3(q) * 2^(byte - 127)) ("[mxfp8 moe training] fix mxfp8 a2a
+    bench script; ...", Summary: the dequantise step of the mxfp8 all-to-all
+    pipeline; E8M0 per the OCP MX spec). Byte 0xFF or an E4M3 NaN code gives
+    the quiet NaN 0x7FC0."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    M, K = q.shape
+    if K % 32 != 0 or s.shape != (M, K // 32):
+        raise ValueError("oracle mx dequant: K % 32 == 0 and scales (M, K/32) required")
+    y = np.empty((M, K), dtype=np.uint16)
+    rc = _load().oracle_mx_dequant_dim0(_ptr(q, ctypes.c_uint8), _ptr(s, ctypes.c_uint8), M, K,
+                                        _ptr(y, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError("oracle mx dequant: bad shape")
+    return y

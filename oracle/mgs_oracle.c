@@ -303,3 +303,61 @@ int oracle_mx_quant_dim0(const uint16_t *x, int64_t M, int64_t K, int mode,
     fpenv_leave(env);
     return 0;
 }
+
+/* ---- MX dequantisation -------------------------------------------------- */
+
+uint16_t oracle_f64_to_bf16(double v)
+{
+    /* Round an exact value once, to nearest even, onto the bf16 grid
+     * (8 significant bits, exponents -126..127, subnormal step 2^-133);
+     * magnitudes from (2 - 2^-8) * 2^127 up round to infinity. NaN gives
+     * the quiet NaN 0x7FC0. */
+    uint16_t sign;
+    double a, quantum, r;
+    int e;
+    float f;
+    uint32_t w;
+    if (v != v)
+        return 0x7FC0;
+    sign = signbit(v) ? 0x8000 : 0;
+    a = fabs(v);
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127))
+        return sign | 0x7F80;
+    if (a < ldexp(1.0, -126)) {
+        quantum = ldexp(1.0, -133);
+    } else {
+        frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+        quantum = ldexp(1.0, e - 1 - 7);
+    }
+    r = rint(a / quantum) * quantum;  /* rint: nearest, ties to even */
+    f = (float)r;                     /* exact: r is on the bf16 grid */
+    memcpy(&w, &f, sizeof w);
+    return sign | (uint16_t)(w >> 16);
+}
+
+int oracle_mx_dequant_dim0(const uint8_t *q, const uint8_t *scales, int64_t M, int64_t K,
+                           uint16_t *y)
+{
+    /* y = bf16(E4M3(q) * 2^(byte - 127)) per block of 32 along a row (the
+     * receiving side of the quantise -> all-to-all -> dequantise pipeline).
+     * E8M0 byte 0xFF is NaN (OCP MX), and so is an E4M3 NaN code: both give
+     * 0x7FC0. The product of a 4-bit significand and a power of two is exact
+     * in binary64, so the one rounding is the cast to bf16. */
+    unsigned env;
+    int64_t r, k, nb;
+    if (M < 0 || K < 0 || K % 32 != 0)
+        return -1;
+    nb = K / 32;
+    env = fpenv_enter();
+    for (r = 0; r < M; ++r)
+        for (k = 0; k < K; ++k) {
+            const uint8_t s = scales[r * nb + k / 32];
+            const double d = oracle_e4m3_decode(q[r * K + k]);
+            if (s == 0xFF || d != d)
+                y[r * K + k] = 0x7FC0;
+            else
+                y[r * K + k] = oracle_f64_to_bf16(d * ldexp(1.0, (int)s - 127));
+        }
+    fpenv_leave(env);
+    return 0;
+}

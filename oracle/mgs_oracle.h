@@ -85,6 +85,16 @@ int oracle_mx_exponent(float amax, int mode);
 int oracle_mx_quant_dim0(const uint16_t *x, int64_t M, int64_t K, int mode,
                          uint8_t *q, uint8_t *scales);
 
+/* bf16 rounding (nearest even, overflow to infinity) of an exact value. */
+uint16_t oracle_f64_to_bf16(double v);
+
+/* MX dequantisation: y (M, K) bf16 = E4M3(q) * 2^(byte - 127) per block of
+ * 32 along K ([MXA2A] Summary: the dequantise step after the all-to-all;
+ * OCP MX E8M0). Byte 0xFF or a NaN code gives 0x7FC0. Returns -1 unless
+ * K % 32 == 0. */
+int oracle_mx_dequant_dim0(const uint8_t *q, const uint8_t *scales, int64_t M, int64_t K,
+                           uint16_t *y);
+
 #ifdef __cplusplus
 }
 #endif
