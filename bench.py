@@ -270,7 +270,8 @@ def main():
 KERNELS = (("copy_kernel", "copy"), ("dim0_kernel", "dim0_kernel"),
            ("dim0t_kernel", "dim0t_kernel"),
            ("dim0_epoch_bump_kernel", "dim0_epoch_bump_kernel"),
-           ("dim1_kernel", "dim1_kernel"), ("mx_kernel", "mx_kernel"))
+           ("dim1_kernel", "dim1_kernel"), ("mx_dequant_kernel", "mx_dequant_kernel"),
+           ("mx_kernel", "mx_kernel"))
 COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -455,6 +456,25 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
         q, s = mgs.mgs_mx_quant_dim0(x5, mode)
         add(c5.name + " " + nm, "mx", c5.x, None, c5.algorithmic_bytes(),
             lambda: (lambda: mgs.mgs_mx_quant_dim0(x5, mode, q=q, scales=s)))
+    # the receiving side: E4M3 + E8M0 back to bf16 (1 + 1/32 B read, 2 B written
+    # per element), then the whole pipeline of the mxfp8 all-to-all with a
+    # device copy of q and scales standing in for the all-to-all
+    n5 = c5.x.size
+    q, s = mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL)
+    y5 = mgs.mgs_mx_dequant_dim0(q, s)
+    add("mx dequant (131072,5120) -> bf16", "mx_dequant", None, None, 3 * n5 + n5 // 32,
+        lambda: (lambda: mgs.mgs_mx_dequant_dim0(q, s, y=y5)))
+    q2, s2 = torch.empty_like(q), torch.empty_like(s)
+
+    def pipeline():
+        mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q, scales=s)
+        mgs.mgs_copy(q, q2)
+        mgs.mgs_copy(s, s2)
+        mgs.mgs_mx_dequant_dim0(q2, s2, y=y5)
+    pipe_bytes = (3 * n5 + n5 // 32) + 2 * (n5 + n5 // 32) + (3 * n5 + n5 // 32)
+    add("mx RCEIL quant -> copy -> dequant (131072,5120)", "mx_pipeline", None, None, pipe_bytes,
+        lambda: pipeline)
+    del q2, s2, y5
     # calibration: plain copy of the same byte count as the target's bf16 input
     src = torch.empty(T.size * 2, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)

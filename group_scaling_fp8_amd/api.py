@@ -129,6 +129,28 @@ def mgs_mx_quant_dim0(x: torch.Tensor, mode: int = MGS_MX_FLOOR,
     return q, scales
 
 
+def mgs_mx_dequant_dim0(q: torch.Tensor, scales: torch.Tensor, y: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """MX dequantisation: q (M, K) E4M3 bytes (uint8 or float8_e4m3fn),
+    scales (M, K/32) E8M0 bytes. Returns y (M, K) bf16 (torch.bfloat16),
+    y = E4M3(q) * 2^(byte - 127) rounded to nearest even."""
+    _need(q, "q", (torch.uint8, torch.float8_e4m3fn), 2)
+    _need(scales, "scales", (torch.uint8,), 2)
+    M, K = q.shape
+    if tuple(scales.shape) != (M, K // 32):
+        raise ValueError("scales has shape %s, expected %s" % (tuple(scales.shape), (M, K // 32)))
+    if y is None:
+        y = torch.empty((M, K), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(y, "y", _BF16_LIKE, 2)
+        if tuple(y.shape) != (M, K):
+            raise ValueError("y has shape %s, expected %s" % (tuple(y.shape), (M, K)))
+    st = lib().mgs_mx_dequant_dim0(q.data_ptr(), scales.data_ptr(), M, K, y.data_ptr(),
+                                   _stream_handle(stream))
+    check("mgs_mx_dequant_dim0", st)
+    return y
+
+
 def mgs_cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """E4M3 cast of a float32 tensor (numel % 4 == 0) with the library's cast."""

@@ -263,6 +263,17 @@ int mgs_mx_quant_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
+int mgs_mx_dequant_dim0(const void* q, const uint8_t* scales_e8m0, int64_t M, int64_t K, void* y,
+                        void* stream) {
+    if (M < 0 || K < 0 || K % 32 != 0) return MGS_ERR_INVALID_ARG;
+    if (M == 0 || K == 0) return MGS_OK;
+    if (M > INT64_MAX / K) return MGS_ERR_UNSUPPORTED;
+    if (!q || !scales_e8m0 || !y || !aligned(q, 16) || !aligned(y, 16)) return MGS_ERR_INVALID_ARG;
+    return hip_status(mgs::launch_mx_dequant(static_cast<const uint8_t*>(q), scales_e8m0, M * K,
+                                             static_cast<uint16_t*>(y),
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
 int mgs_cast_e4m3(const float* in, int64_t n, uint8_t* out, void* stream) {
     if (n < 0 || n % 4 != 0) return MGS_ERR_INVALID_ARG;
     if (n == 0) return MGS_OK;

@@ -29,6 +29,9 @@ hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, 
 hipError_t launch_mx(const uint16_t* x, int64_t n_elems, bool rceil, uint8_t* q, uint8_t* scales,
                      hipStream_t stream);
 
+hipError_t launch_mx_dequant(const uint8_t* q, const uint8_t* scales, int64_t n_elems, uint16_t* y,
+                             hipStream_t stream);
+
 hipError_t launch_cast(const float* in, int64_t n, uint8_t* out, hipStream_t stream);
 
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);

@@ -179,6 +179,20 @@ int mgs_mx_quant_dim0(const void *x, int64_t M, int64_t K,
  * saturate to 0x7E / 0xFE; NaN inputs are outside the contract.
  * Requirements: n % 4 == 0, in 16-byte aligned, out 4-byte aligned.
  */
+/*
+ * MX dequantisation along the last dim ([MXA2A] Summary: the dequantise step
+ * that follows the all-to-all of mxfp8-quantised tokens; OCP MX E8M0):
+ *   q            (M, K) E4M3 bytes, K % 32 == 0.
+ *   scales_e8m0  (M, K/32) bytes; block b of row r covers q[r, 32b .. 32b+31].
+ *   y            (M, K) bf16, written: y = bf16(E4M3(q) * 2^(byte - 127)),
+ *                rounded to nearest even (the product itself is exact);
+ *                overflow gives infinity. Byte 0xFF (E8M0 NaN) or an E4M3 NaN
+ *                code gives the quiet NaN 0x7FC0.
+ * Requirements: q and y 16-byte aligned. M == 0 or K == 0 is a no-op.
+ */
+int mgs_mx_dequant_dim0(const void *q, const uint8_t *scales_e8m0, int64_t M,
+                        int64_t K, void *y, void *stream);
+
 int mgs_cast_e4m3(const float *in, int64_t n, uint8_t *out, void *stream);
 
 /*

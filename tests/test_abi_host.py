@@ -86,6 +86,19 @@ def test_grouped_argument_errors(L, fn):
         assert call(K=mgs._lib.MGS_DIM1_MAX_K + 16) == UNSUPPORTED
 
 
+def test_mx_dequant_argument_errors(L):
+    f = L.mgs_mx_dequant_dim0
+    assert f(A, A, 4, 48, A, None) == INVALID            # K % 32
+    assert f(A, A, -1, 64, A, None) == INVALID
+    assert f(None, A, 4, 64, A, None) == INVALID
+    assert f(A, None, 4, 64, A, None) == INVALID
+    assert f(A, A, 4, 64, None, None) == INVALID
+    assert f(A + 8, A, 4, 64, A, None) == INVALID         # q 16-byte aligned
+    assert f(A, A, 4, 64, A + 8, None) == INVALID         # y 16-byte aligned
+    assert f(A, A, 0, 64, A, None) == mgs.MGS_OK
+    assert f(A, A, 1 << 40, 1 << 30, A, None) == UNSUPPORTED
+
+
 def test_mx_argument_errors(L):
     f = L.mgs_mx_quant_dim0
     assert f(A, 4, 48, None, 0, 0, A, A, None) == INVALID           # K % 32
