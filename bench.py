@@ -450,6 +450,15 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
     add("dim0_t (16640,8192) G=64 -> (8192,16640)", "dim0_t", T, w.offsets, w.algorithmic_bytes(),
         lambda: (lambda: mgs.mgs_quant_groups_dim0_t(xt6, ot6, q_t=qt6, scales_t=st6)))
     del w, xt6, ot6, qt6, st6
+    # per-expert scaling of a 3D weight along dim 1: 16 experts of (5120, 8192),
+    # each expert a 5120-row group cut into 8-chunk teams (seeded on the GPU)
+    E, D1, D2 = 16, 5120, 8192
+    gen = torch.Generator(device=dev).manual_seed(7)
+    w3 = (torch.randn((E, D1, D2), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    q3, s3 = mgs.mgs_quant_experts_dim1(w3)
+    add("experts (16,5120,8192) along dim1", "experts", None, None, 3 * E * D1 * D2 + 4 * E * D2,
+        lambda: (lambda: mgs.mgs_quant_experts_dim1(w3, q=q3, scales=s3)))
+    del w3, q3, s3
     c5 = wl.c5_mx()
     x5 = torch.from_numpy(c5.x.view(np.int16)).to(dev)
     for mode, nm in ((mgs.MGS_MX_FLOOR, "FLOOR"), (mgs.MGS_MX_RCEIL, "RCEIL")):

@@ -15,5 +15,5 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     mgs_cast_e4m3, mgs_copy, mgs_mx_dequant_dim0, mgs_mx_quant_dim0, mgs_quant_groups_dim0, mgs_quant_groups_dim0_t,
-    mgs_quant_groups_dim1,
+    mgs_quant_experts_dim1, mgs_quant_groups_dim1,
 )

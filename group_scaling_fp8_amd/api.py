@@ -88,6 +88,21 @@ def mgs_quant_groups_dim0_t(x: torch.Tensor, offsets: torch.Tensor, pow2: bool =
     return q_t, scales_t
 
 
+def mgs_quant_experts_dim1(w: torch.Tensor, pow2: bool = False, q: Optional[torch.Tensor] = None,
+                           scales: Optional[torch.Tensor] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-expert scaling of a 3D weight w (E, D1, D2) bf16 along dim 1.
+    Returns q (E, D1, D2) uint8 E4M3 and scales (E, D2) float32."""
+    _need(w, "w", _BF16_LIKE, 3)
+    E, D1, D2 = w.shape
+    q = _out(q, (E, D1, D2), torch.uint8, w.device, "q")
+    scales = _out(scales, (E, D2), torch.float32, w.device, "scales")
+    st = lib().mgs_quant_experts_dim1(w.data_ptr(), E, D1, D2, MGS_FLAG_POW2_SCALE if pow2 else 0,
+                                      q.data_ptr(), scales.data_ptr(), _stream_handle(stream))
+    check("mgs_quant_experts_dim1", st)
+    return q, scales
+
+
 def mgs_quant_groups_dim1(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
                           q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
                           stream=None, validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -110,6 +110,10 @@ int validate_offsets(const int32_t* offsets, int32_t n_groups, int64_t extent, i
     return prev == extent ? MGS_OK : MGS_ERR_INVALID_ARG;
 }
 
+// A stand-in for the offsets pointer of calls that have none (equal groups):
+// well aligned, never dereferenced.
+const int32_t* const kNoOffsets = reinterpret_cast<const int32_t*>(uintptr_t(256));
+
 int check_grouped(const void* x, int64_t M, int64_t K, const int32_t* offsets, int32_t n_groups,
                   uint32_t flags, const void* q, const float* scales) {
     if (M < 0 || K < 0) return MGS_ERR_INVALID_ARG;
@@ -173,16 +177,18 @@ int dim0_team_max(const DeviceInfo& d) {
 }
 
 // Both dim0 entry points: q (M, K) and scales (G, K), or their transposes.
+// uniform_rows >= 0: n_groups equal groups of uniform_rows rows and no offsets.
 int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
                       int32_t n_groups, uint32_t flags, void* q, float* scales, void* stream,
-                      bool transposed) {
-    int st = check_grouped(x, M, K, offsets, n_groups, flags, q, scales);
+                      bool transposed, int64_t uniform_rows = -1) {
+    const bool uniform = uniform_rows >= 0;
+    int st = check_grouped(x, M, K, uniform ? kNoOffsets : offsets, n_groups, flags, q, scales);
     if (st != MGS_OK) return st;
     if (K % 8 != 0) return MGS_ERR_INVALID_ARG;
     if (transposed && (M % 16 != 0 || (M * K > 0 && !aligned(q, 16)))) return MGS_ERR_INVALID_ARG;
     if (K == 0) return MGS_OK;
     if (!scales || !aligned(scales, transposed ? 4 : 16)) return MGS_ERR_INVALID_ARG;
-    if (flags & MGS_FLAG_VALIDATE) {
+    if ((flags & MGS_FLAG_VALIDATE) && !uniform) {
         st = validate_offsets(offsets, n_groups, M, transposed ? 16 : 1,
                               reinterpret_cast<hipStream_t>(stream));
         if (st != MGS_OK) return st;
@@ -209,7 +215,8 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
         }
     }
     return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, (int)K, offsets,
-                                       n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0, transposed,
+                                       n_groups, (int)uniform_rows,
+                                       (flags & MGS_FLAG_POW2_SCALE) != 0, transposed,
                                        static_cast<uint8_t*>(q), scales, team_max, ws, gen,
                                        mgs::dim0_spin_ticks(dinfo), s));
 }
@@ -228,6 +235,14 @@ int mgs_quant_groups_dim0_t(const void* x, int64_t M, int64_t K, const int32_t* 
                             int32_t n_groups, uint32_t flags, void* q_t, float* scales_t,
                             void* stream) {
     return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q_t, scales_t, stream, true);
+}
+
+int mgs_quant_experts_dim1(const void* w, int64_t E, int64_t D1, int64_t D2, uint32_t flags,
+                           void* q, float* scales, void* stream) {
+    if (E < 1 || D1 < 0) return MGS_ERR_INVALID_ARG;
+    if (E > MGS_MAX_GROUPS || D1 > INT32_MAX / E) return MGS_ERR_UNSUPPORTED;
+    return mgs::quant_groups_dim0(w, E * D1, D2, nullptr, (int32_t)E, flags, q, scales, stream, false,
+                                  D1);
 }
 
 int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* offsets,

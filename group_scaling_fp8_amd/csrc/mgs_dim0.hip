@@ -161,8 +161,10 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
 
 // Tile number `target` of the order described at the top of this file. Run
 // by every wave of the workgroup; all lanes return the same tile.
+// Group ends come from off (uniform_rows < 0), or are (g + 1) * uniform_rows
+// (equal groups, e.g. the experts of a 3D weight, with no offsets array).
 __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
-                          int lt_cap, bool maybe_c, int row_align, int target) {
+                          int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target) {
     const int lane = threadIdx.x & (kWave - 1);
     Tile t;
     t.g = -1;
@@ -171,7 +173,9 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
     int carry_end = 0, carry_x = 0, carry_m = 0, carry_ch = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
-        const int raw = min(max(g < G ? off[g] : M, 0), M) & -row_align;
+        const int raw =
+            min(max(g < G ? (uniform_rows >= 0 ? (g + 1) * uniform_rows : off[g]) : M, 0), M) &
+            -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         // the previous lane's end (wave_shr:1); lane 0 keeps carry_end
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
@@ -211,7 +215,9 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
     carry_end = carry_m = carry_ch = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
-        const int raw = min(max(g < G ? off[g] : M, 0), M) & -row_align;
+        const int raw =
+            min(max(g < G ? (uniform_rows >= 0 ? (g + 1) * uniform_rows : off[g]) : M, 0), M) &
+            -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
         const GroupInfo gi = group_info(start, end, g < G, K, team_max, lt_cap);
@@ -414,12 +420,13 @@ __device__ __forceinline__ void dim0_body(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks, uint4* red, uint32_t* stage) {
+        uint32_t gen_arg, long long spin_ticks, int uniform_rows, uint4* red, uint32_t* stage) {
     constexpr int kRowAlign = kT ? 16 : 1;
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign, (int)item);
+        const Tile t = find_tile(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign, uniform_rows,
+                                 (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);
         const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
@@ -567,10 +574,10 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks) {
+        uint32_t gen_arg, long long spin_ticks, int uniform_rows) {
     __shared__ uint4 red[kThreads];
     dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
-                     ws_max, gen_arg, spin_ticks, red, nullptr);
+                     ws_max, gen_arg, spin_ticks, uniform_rows, red, nullptr);
 }
 
 // The same per-group scaling with transposed outputs: qT (K, M), scalesT (K, G).
@@ -578,11 +585,11 @@ __global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks) {
+        uint32_t gen_arg, long long spin_ticks, int uniform_rows) {
     __shared__ uint4 red[kThreads];
     __shared__ uint4 stage[kStageWords / 4];
     dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
-                    ws_max, gen_arg, spin_ticks, red, reinterpret_cast<uint32_t*>(stage));
+                    ws_max, gen_arg, spin_ticks, uniform_rows, red, reinterpret_cast<uint32_t*>(stage));
 }
 
 // Advances the epoch word by one, keeping its top bit set so that epochs
@@ -595,8 +602,8 @@ __global__ void dim0_epoch_bump_kernel(uint32_t* __restrict__ ws_epoch) {
     }
 }
 
-hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, bool pow2,
-                       bool transposed, uint8_t* q, float* scales, int team_max, void* ws,
+hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
+                       bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, void* ws,
                        uint32_t gen, long long spin_ticks, hipStream_t stream) {
     const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
@@ -613,7 +620,7 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
     const int maybe_c = (int64_t)M > (int64_t)kRowsW128 * team_max ? 1 : 0;
     hipLaunchKernelGGL(transposed ? dim0t_kernel : dim0_kernel, dim3((unsigned)grid), dim3(kThreads),
                        0, stream, x, M, K, off, G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max,
-                       lt_cap, maybe_c, ws_epoch, ws_max, gen, spin_ticks);
+                       lt_cap, maybe_c, ws_epoch, ws_max, gen, spin_ticks, uniform_rows);
     return hipGetLastError();
 }
 

@@ -136,6 +136,26 @@ int mgs_quant_groups_dim0_t(const void *x, int64_t M, int64_t K,
                             void *stream);
 
 /*
+ * Per-expert scaling of a 3D expert weight along its dim 1 ([ROWWISE]'s
+ * stacked changes: a fused reduction kernel along dim1 for 3d expert weights
+ * in the backward pass; [BLOCKSIZE]'s: fp8 rowwise kernels for expert
+ * weights). Reading: one scale per (expert, column), from the amax over the
+ * expert's D1 rows, fused with the cast -- dim0's per-group scaling of the
+ * (E * D1, D2) view with E equal groups of D1 rows, and no offsets array.
+ *   w       (E, D1, D2) bf16.
+ *   flags   0 or MGS_FLAG_POW2_SCALE (MGS_FLAG_VALIDATE is accepted and
+ *           has nothing to check).
+ *   q       (E, D1, D2) E4M3 bytes, written.
+ *   scales  (E, D2) fp32, written.
+ * Requirements: 1 <= E <= 1024, D1 >= 0, E * D1 < 2^31, D2 % 8 == 0; w
+ * 16-byte aligned, q 8-byte aligned, scales 16-byte aligned. Experts taller
+ * than 640 rows are cut into chunks exactly as dim0's groups (workspace,
+ * bounded wait and graph capture as for mgs_quant_groups_dim0).
+ */
+int mgs_quant_experts_dim1(const void *w, int64_t E, int64_t D1, int64_t D2,
+                           uint32_t flags, void *q, float *scales, void *stream);
+
+/*
  * Per-group rowwise scaling along dim1 ([ROWWISE] Summary).
  *   x       (M, K) bf16. Groups split the K columns.
  *   offsets n_groups int32 end offsets along K. Every offset must be a

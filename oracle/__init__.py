@@ -163,6 +163,19 @@ def quant_groups_dim0_t(x_bits: np.ndarray, offsets: np.ndarray, pow2: bool = Fa
     return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
 
 
+def quant_experts_dim1(w_bits: np.ndarray, pow2: bool = False):
+    """w (E, D1, D2) bf16 bits -> (q (E, D1, D2) u8, scales (E, D2) f32): one
+    scale per (expert, column) from the amax over the expert's D1 rows (the
+    fused dim1 reduction for 3D expert weights named in the stacked changes
+    of "[moe fp8 training] test and bench new faster method for per group
+    rowwise scaling"). By definition this is per-group scaling along dim0 of
+    the (E * D1, D2) view with E equal groups of D1 rows."""
+    E, D1, D2 = w_bits.shape
+    off = (np.arange(1, E + 1, dtype=np.int64) * D1).astype(np.int32)
+    q, s = quant_groups_dim0(np.ascontiguousarray(w_bits).reshape(E * D1, D2), off, pow2)
+    return q.reshape(E, D1, D2), s
+
+
 def quant_groups_dim1(x_bits: np.ndarray, offsets: np.ndarray, pow2: bool = False):
     """x (M, K) bf16 bits, int32 end offsets along K -> (q (M, K) u8, scales (M, G) f32)."""
     x = _bf16_bits(x_bits)

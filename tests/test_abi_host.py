@@ -86,6 +86,20 @@ def test_grouped_argument_errors(L, fn):
         assert call(K=mgs._lib.MGS_DIM1_MAX_K + 16) == UNSUPPORTED
 
 
+def test_experts_argument_errors(L):
+    f = L.mgs_quant_experts_dim1
+    assert f(A, 0, 64, 128, 0, A, A, None) == INVALID        # E >= 1
+    assert f(A, 2, -1, 128, 0, A, A, None) == INVALID
+    assert f(A, 1025, 16, 128, 0, A, A, None) == UNSUPPORTED
+    assert f(A, 4, 1 << 30, 128, 0, A, A, None) == UNSUPPORTED   # E * D1 >= 2^31
+    assert f(A, 2, 64, 12, 0, A, A, None) == INVALID         # D2 % 8
+    assert f(A, 2, 64, 128, 4, A, A, None) == INVALID        # unknown flag
+    assert f(A + 8, 2, 64, 128, 0, A, A, None) == INVALID
+    assert f(A, 2, 64, 128, 0, A + 4, A, None) == INVALID
+    assert f(A, 2, 64, 128, 0, A, A + 4, None) == INVALID
+    assert f(None, 2, 64, 128, 0, A, A, None) == INVALID
+
+
 def test_mx_dequant_argument_errors(L):
     f = L.mgs_mx_dequant_dim0
     assert f(A, A, 4, 48, A, None) == INVALID            # K % 32

@@ -223,6 +223,25 @@ def test_dim0_transposed_is_dim1_of_the_transpose(oracle_mod, pow2):
     assert np.array_equal(st.view(np.uint32), s1.view(np.uint32))
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_expert_weights_dim1_by_brute_force(oracle_mod, pow2):
+    """quant_experts_dim1 against a direct per-(expert, column) computation:
+    the column amax of each expert through numpy, the scale from the oracle's
+    pinned group_scale, and each element through the pinned E4M3 encoder."""
+    rng = np.random.default_rng(47)
+    w = wl.randn_bf16(rng, (3, 21, 16), 0.02, 0.01, 8.0).reshape(3, 21, 16)
+    q, s = oracle_mod.quant_experts_dim1(w, pow2)
+    wf = wl.bf16_bits_to_f32(w)
+    for e in range(3):
+        for k in range(16):
+            amax = np.float32(np.max(np.abs(wf[e, :, k])))
+            sc = np.float32(oracle_mod.group_scale(float(amax), pow2))
+            assert np.float32(s[e, k]) == sc
+            for r in range(21):
+                v = float(np.float32(wf[e, r, k]) * sc)
+                assert q[e, r, k] == oracle_mod.e4m3_encode(v)
+
+
 def test_bad_offsets_rejected(oracle_mod):
     x = np.zeros((32, 16), np.uint16)
     for off in ([16, 8, 32], [16, 31], [33], [-1, 32]):
