@@ -271,6 +271,7 @@ KERNELS = (("copy_kernel", "copy"), ("dim0_kernel", "dim0_kernel"),
            ("dim0t_kernel", "dim0t_kernel"),
            ("dim0_epoch_bump_kernel", "dim0_epoch_bump_kernel"),
            ("dim1_kernel", "dim1_kernel"), ("mx_dequant_kernel", "mx_dequant_kernel"),
+           ("mx_dim1_kernel", "mx_dim1_kernel"),
            ("mx_kernel", "mx_kernel"))
 COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
 
@@ -465,6 +466,11 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
         q, s = mgs.mgs_mx_quant_dim0(x5, mode)
         add(c5.name + " " + nm, "mx", c5.x, None, c5.algorithmic_bytes(),
             lambda: (lambda: mgs.mgs_mx_quant_dim0(x5, mode, q=q, scales=s)))
+    # blocks of 32 along dim0, GEMM-ready transposed outputs (K, M) and (K, M/32)
+    qd1, sd1 = mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR)
+    add("mx dim1 (131072,5120) FLOOR -> (5120,131072)", "mx_dim1", c5.x, None, c5.algorithmic_bytes(),
+        lambda: (lambda: mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR, q_t=qd1, scales_t=sd1)))
+    del qd1, sd1
     # the receiving side: E4M3 + E8M0 back to bf16 (1 + 1/32 B read, 2 B written
     # per element), then the whole pipeline of the mxfp8 all-to-all with a
     # device copy of q and scales standing in for the all-to-all

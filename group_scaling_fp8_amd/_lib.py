@@ -22,7 +22,7 @@ MGS_DIM1_MAX_K = 131072
 EXPORTS = (
     "mgs_quant_groups_dim0", "mgs_quant_groups_dim0_t", "mgs_quant_experts_dim1",
     "mgs_quant_groups_dim1", "mgs_mx_quant_dim0",
-    "mgs_mx_dequant_dim0", "mgs_cast_e4m3",
+    "mgs_mx_quant_dim1", "mgs_mx_dequant_dim0", "mgs_cast_e4m3",
     "mgs_copy", "mgs_status_string", "mgs_last_hip_error",
 )
 
@@ -62,6 +62,8 @@ def lib():
         L.mgs_mx_quant_dim0.restype = ctypes.c_int
         L.mgs_quant_experts_dim1.argtypes = [vp, i64, i64, i64, u32, vp, vp, vp]
         L.mgs_quant_experts_dim1.restype = ctypes.c_int
+        L.mgs_mx_quant_dim1.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp]
+        L.mgs_mx_quant_dim1.restype = ctypes.c_int
         L.mgs_mx_dequant_dim0.argtypes = [vp, vp, i64, i64, vp, vp]
         L.mgs_mx_dequant_dim0.restype = ctypes.c_int
         L.mgs_cast_e4m3.argtypes = [vp, i64, vp, vp]

@@ -144,6 +144,22 @@ def mgs_mx_quant_dim0(x: torch.Tensor, mode: int = MGS_MX_FLOOR,
     return q, scales
 
 
+def mgs_mx_quant_dim1(x: torch.Tensor, mode: int = MGS_MX_FLOOR, q_t: Optional[torch.Tensor] = None,
+                      scales_t: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MX block-32 cast along dim0 with transposed outputs: x (M, K) bf16,
+    M % 32 == 0. Returns q_t (K, M) uint8 E4M3 and scales_t (K, M/32) uint8
+    E8M0 -- mgs_mx_quant_dim0 of x^T."""
+    _need(x, "x", _BF16_LIKE, 2)
+    M, K = x.shape
+    q_t = _out(q_t, (K, M), torch.uint8, x.device, "q_t")
+    scales_t = _out(scales_t, (K, M // 32), torch.uint8, x.device, "scales_t")
+    st = lib().mgs_mx_quant_dim1(x.data_ptr(), M, K, int(mode), q_t.data_ptr(), scales_t.data_ptr(),
+                                 _stream_handle(stream))
+    check("mgs_mx_quant_dim1", st)
+    return q_t, scales_t
+
+
 def mgs_mx_dequant_dim0(q: torch.Tensor, scales: torch.Tensor, y: Optional[torch.Tensor] = None,
                         stream=None) -> torch.Tensor:
     """MX dequantisation: q (M, K) E4M3 bytes (uint8 or float8_e4m3fn),

@@ -278,6 +278,18 @@ int mgs_mx_quant_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
+int mgs_mx_quant_dim1(const void* x, int64_t M, int64_t K, int mode, void* q_t, uint8_t* scales_t,
+                      void* stream) {
+    if (M < 0 || K < 0 || M % 32 != 0 || K % 8 != 0) return MGS_ERR_INVALID_ARG;
+    if (mode != MGS_MX_FLOOR && mode != MGS_MX_RCEIL) return MGS_ERR_INVALID_ARG;
+    if (M == 0 || K == 0) return MGS_OK;
+    if (M > INT64_MAX / K) return MGS_ERR_UNSUPPORTED;
+    if (!x || !q_t || !scales_t || !aligned(x, 16) || !aligned(q_t, 8)) return MGS_ERR_INVALID_ARG;
+    return hip_status(mgs::launch_mx_dim1(static_cast<const uint16_t*>(x), M, K, mode == MGS_MX_RCEIL,
+                                          static_cast<uint8_t*>(q_t), scales_t,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
 int mgs_mx_dequant_dim0(const void* q, const uint8_t* scales_e8m0, int64_t M, int64_t K, void* y,
                         void* stream) {
     if (M < 0 || K < 0 || K % 32 != 0) return MGS_ERR_INVALID_ARG;

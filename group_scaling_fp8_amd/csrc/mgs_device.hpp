@@ -74,6 +74,24 @@ __device__ __forceinline__ void store_stream(void* p, uint2 v) {
     __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
 }
 
+// ---- byte transposes ----------------------------------------------------------
+
+// Byte transpose of a 4 x 4 block: a, b, c, d hold bytes 0..3 of four
+// consecutive rows; word j of out holds byte j of a, b, c, d (low to high).
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                             uint32_t (&out)[4]) {
+    // v_perm_b32 picks bytes of {hi, lo}: selector bytes 0..3 address lo,
+    // 4..7 address hi
+    const uint32_t ab01 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+    const uint32_t ab23 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+    const uint32_t cd01 = __builtin_amdgcn_perm(d, c, 0x05010400u);
+    const uint32_t cd23 = __builtin_amdgcn_perm(d, c, 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(cd01, ab01, 0x05040100u);           // a0 b0 c0 d0
+    out[1] = __builtin_amdgcn_perm(cd01, ab01, 0x07060302u);           // a1 b1 c1 d1
+    out[2] = __builtin_amdgcn_perm(cd23, ab23, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(cd23, ab23, 0x07060302u);
+}
+
 // ---- per-group scale ---------------------------------------------------------
 
 // amax15 is the bf16 magnitude pattern of the group's max |x|.

@@ -30,6 +30,11 @@ hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, 
 hipError_t launch_mx(const uint16_t* x, int64_t n_elems, bool rceil, uint8_t* q, uint8_t* scales,
                      hipStream_t stream);
 
+// blocks of 32 along dim0 (M % 32 == 0), outputs transposed: q_t (K, M),
+// scales_t (K, M/32)
+hipError_t launch_mx_dim1(const uint16_t* x, int64_t M, int64_t K, bool rceil, uint8_t* q_t,
+                          uint8_t* scales_t, hipStream_t stream);
+
 hipError_t launch_mx_dequant(const uint8_t* q, const uint8_t* scales, int64_t n_elems, uint16_t* y,
                              hipStream_t stream);
 

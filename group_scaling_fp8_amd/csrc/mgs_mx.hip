@@ -57,6 +57,109 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const uint16_t* __restrict
     }
 }
 
+// ---- MX cast along dim0 (blocks of 32 rows), transposed output ------------------
+// The MX cast of x^T computed from x: q_t (K, M) E4M3 with blocks of 32 along
+// its rows and scales_t (K, M/32), the GEMM-ready form. A 256-thread workgroup
+// takes 128 rows x 128 columns; a lane holds 8 consecutive rows of 8 columns,
+// so each wave covers exactly one block of 32 rows and a column's block amax
+// is two lane swaps (the four lanes of the wave that share its columns). A
+// lane casts its 8 x 8 block and transposes it in registers; the tile goes
+// through 16 KiB of LDS so that q_t is written in whole 128-byte pieces of
+// its rows (eight lanes each), and the scales in runs of a column's blocks.
+constexpr int kMxTile = 128;
+
+__global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                           int64_t K, int rceil,
+                                                           uint8_t* __restrict__ q_t,
+                                                           uint8_t* __restrict__ scales_t) {
+    const int64_t nm = (M + kMxTile - 1) / kMxTile;
+    const int64_t tile_m = blockIdx.x % nm, tile_k = blockIdx.x / nm;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;        // 16 column groups, 16 row groups
+    const int64_t row0 = tile_m * kMxTile + 8 * ty;                // this lane's 8 rows
+    const int64_t col = tile_k * kMxTile + 8 * tx;                  // and 8 columns
+    // M % 32 == 0 and K % 8 == 0: a wave's block and a lane's columns are whole
+    const bool ok = row0 < M && col < K;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (ok) v[i] = load_stream(x + (row0 + i) * K + col);
+    }
+    // column magnitudes over this lane's rows, then over the wave's four row groups
+    uint4 m = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        m.x = mag_max2(m.x, v[i].x);
+        m.y = mag_max2(m.y, v[i].y);
+        m.z = mag_max2(m.z, v[i].z);
+        m.w = mag_max2(m.w, v[i].w);
+    }
+#pragma unroll
+    for (int d = 16; d < kWave; d <<= 1) {
+        m.x = mag_max2(m.x, (uint32_t)__shfl_xor((int)m.x, d, kWave));
+        m.y = mag_max2(m.y, (uint32_t)__shfl_xor((int)m.y, d, kWave));
+        m.z = mag_max2(m.z, (uint32_t)__shfl_xor((int)m.z, d, kWave));
+        m.w = mag_max2(m.w, (uint32_t)__shfl_xor((int)m.w, d, kWave));
+    }
+    const uint32_t a[8] = {m.x & 0xFFFFu, m.x >> 16, m.y & 0xFFFFu, m.y >> 16,
+                           m.z & 0xFFFFu, m.z >> 16, m.w & 0xFFFFu, m.w >> 16};
+    uint32_t byte[8];
+    float mult[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int b = (int)(a[j] >> 7) - 8 + ((rceil != 0 && (a[j] & 0x7Fu) > 96u) ? 1 : 0);
+        byte[j] = (uint32_t)max(b, 0);
+        mult[j] = __uint_as_float((254u - byte[j]) << 23);
+    }
+    // stage the cast tile in LDS as column words (four rows each), the word
+    // index XOR-swizzled with the lane's column block, and the scale bytes as
+    // [column][block]; then store whole 128-byte pieces of q_t rows
+    __shared__ uint32_t st[kMxTile * kMxTile / 4];
+    __shared__ uint8_t sst[kMxTile * 4];
+    const int w = threadIdx.x >> 6;                                 // this wave's block of the tile
+    if (ok) {
+        uint2 r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r[i] = cast8(v[i], mult[0], mult[1], mult[2], mult[3], mult[4], mult[5], mult[6], mult[7]);
+        uint32_t lo03[4], lo47[4], hi03[4], hi47[4];     // columns 0-3 / 4-7, rows 0-3 / 4-7
+        transpose4x4(r[0].x, r[1].x, r[2].x, r[3].x, lo03);
+        transpose4x4(r[4].x, r[5].x, r[6].x, r[7].x, lo47);
+        transpose4x4(r[0].y, r[1].y, r[2].y, r[3].y, hi03);
+        transpose4x4(r[4].y, r[5].y, r[6].y, r[7].y, hi47);
+        const int word = (2 * ty) ^ ((tx & 7) << 2);                // rows 8ty .. 8ty + 7
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<uint2*>(st + (8 * tx + j) * 32 + word) = make_uint2(lo03[j], lo47[j]);
+            *reinterpret_cast<uint2*>(st + (8 * tx + 4 + j) * 32 + word) = make_uint2(hi03[j], hi47[j]);
+        }
+        if ((ty & 3) == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sst[(8 * tx + j) * 4 + w] = (uint8_t)byte[j];
+        }
+    }
+    __syncthreads();
+    const int64_t r0 = tile_m * kMxTile, c0 = tile_k * kMxTile;
+    const int rows = (int)min((int64_t)kMxTile, M - r0);            // a multiple of 32
+    const int cols = (int)min((int64_t)kMxTile, K - c0);            // a multiple of 8
+    const int pieces = rows >> 4;                                    // 16-byte pieces per column
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = threadIdx.x + k * kThreads;                  // 8 pieces per column, pieces fastest
+        const int c = idx >> 3, p = idx & 7;
+        if (c < cols && p < pieces) {
+            const uint4 val = *reinterpret_cast<const uint4*>(st + c * 32 + ((4 * p) ^ (((c >> 3) & 7) << 2)));
+            *reinterpret_cast<uint4*>(q_t + (c0 + c) * M + r0 + 16 * p) = val;
+        }
+    }
+    if (threadIdx.x < cols) {
+        const int c = threadIdx.x;
+        const int64_t nb = M / 32;
+        uint8_t* dst = scales_t + (c0 + c) * nb + r0 / 32;
+        for (int b = 0; b < (rows >> 5); ++b) dst[b] = sst[c * 4 + b];
+    }
+}
+
 // ---- MX dequantisation ------------------------------------------------------
 // y = bf16(E4M3(q) * 2^(byte - 127)) per block of 32: the receiving side of
 // the quantise -> all-to-all -> dequantise pipeline. A lane takes 16 codes
@@ -159,6 +262,15 @@ hipError_t launch_mx(const uint16_t* x, int64_t n_elems, bool rceil, uint8_t* q,
     const int64_t blocks = (n_vec + per_block - 1) / per_block;
     hipLaunchKernelGGL(mx_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, n_vec,
                        rceil ? 1 : 0, q, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_dim1(const uint16_t* x, int64_t M, int64_t K, bool rceil, uint8_t* q_t,
+                          uint8_t* scales_t, hipStream_t stream) {
+    const int64_t tiles = ((M + kMxTile - 1) / kMxTile) * ((K + kMxTile - 1) / kMxTile);
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mx_dim1_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, x, M, K,
+                       rceil ? 1 : 0, q_t, scales_t);
     return hipGetLastError();
 }
 

@@ -200,6 +200,22 @@ int mgs_mx_quant_dim0(const void *x, int64_t M, int64_t K,
  * Requirements: n % 4 == 0, in 16-byte aligned, out 4-byte aligned.
  */
 /*
+ * MX-style block-32 cast along dim0, written transposed (the dim1 form of
+ * [MXA2A]'s cast benchmark modes: blocks of 32 consecutive rows of one
+ * column). The values are mgs_mx_quant_dim0's on x^T, computed from x in
+ * one pass without storing x^T.
+ *   x         (M, K) bf16, M % 32 == 0, K % 8 == 0.
+ *   mode      MGS_MX_FLOOR or MGS_MX_RCEIL (as for mgs_mx_quant_dim0).
+ *   q_t       (K, M) E4M3 bytes: q_t[k, r] is x[r, k] cast with the scale
+ *             of rows 32 * (r / 32) .. + 31 of column k.
+ *   scales_t  (K, M/32) bytes, E8M0 (exponent + 127).
+ * Requirements: x 16-byte aligned, q_t 8-byte aligned. M == 0 or K == 0 is
+ * a no-op.
+ */
+int mgs_mx_quant_dim1(const void *x, int64_t M, int64_t K, int mode,
+                      void *q_t, uint8_t *scales_t, void *stream);
+
+/*
  * MX dequantisation along the last dim ([MXA2A] Summary: the dequantise step
  * that follows the all-to-all of mxfp8-quantised tokens; OCP MX E8M0):
  *   q            (M, K) E4M3 bytes, K % 32 == 0.

@@ -229,3 +229,12 @@ def mx_dequant_dim0(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle mx dequant: bad shape")
     return y
+
+
+def mx_quant_dim1(x_bits: np.ndarray, mode: int):
+    """x (M, K) bf16 bits, M % 32 == 0 -> (q_t (K, M) u8, scales_t (K, M/32)
+    u8 E8M0): blocks of 32 consecutive rows of one column, the outputs in
+    the transposed layout -- by definition mx_quant_dim0 of x^T ("[mxfp8 moe
+    training] fix mxfp8 a2a bench script; ...", investigation comment: the
+    cast benchmark's modes)."""
+    return mx_quant_dim0(np.ascontiguousarray(np.asarray(x_bits).T), mode)

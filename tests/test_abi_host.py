@@ -100,6 +100,17 @@ def test_experts_argument_errors(L):
     assert f(None, 2, 64, 128, 0, A, A, None) == INVALID
 
 
+def test_mx_dim1_argument_errors(L):
+    f = L.mgs_mx_quant_dim1
+    assert f(A, 48, 64, 0, A, A, None) == INVALID           # M % 32
+    assert f(A, 64, 12, 0, A, A, None) == INVALID           # K % 8
+    assert f(A, 64, 64, 2, A, A, None) == INVALID           # mode
+    assert f(A + 8, 64, 64, 0, A, A, None) == INVALID
+    assert f(A, 64, 64, 0, A + 4, A, None) == INVALID
+    assert f(A, 64, 64, 0, A, None, None) == INVALID
+    assert f(A, 0, 64, 0, A, A, None) == mgs.MGS_OK
+
+
 def test_mx_dequant_argument_errors(L):
     f = L.mgs_mx_dequant_dim0
     assert f(A, A, 4, 48, A, None) == INVALID            # K % 32

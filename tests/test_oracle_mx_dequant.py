@@ -76,3 +76,23 @@ def test_round_trip_of_representable_blocks():
 def test_shape_checks():
     with pytest.raises(ValueError):
         oracle.mx_dequant_dim0(np.zeros((2, 48), np.uint8), np.zeros((2, 1), np.uint8))
+
+
+@pytest.mark.parametrize("mode", [oracle.FLOOR, oracle.RCEIL])
+def test_mx_dim1_by_brute_force(mode):
+    """mx_quant_dim1 against a direct per-(column, 32-row block) computation:
+    the block amax by numpy, the exponent from the pinned mx_exponent, and
+    each element through the pinned E4M3 encoder at an exact power of two."""
+    from group_scaling_fp8_amd import workloads as wl
+    rng = np.random.default_rng(53 + mode)
+    x = wl.randn_bf16(rng, (64, 24), 1.0, 0.01, 100.0)
+    q, s = oracle.mx_quant_dim1(x, mode)
+    assert q.shape == (24, 64) and s.shape == (24, 2)
+    xf = wl.bf16_bits_to_f32(x)
+    for k in range(24):
+        for b in range(2):
+            blk = xf[32 * b:32 * b + 32, k]
+            e = oracle.mx_exponent(float(np.max(np.abs(blk))), mode)
+            assert s[k, b] == e + 127
+            for i in range(32):
+                assert q[k, 32 * b + i] == oracle.e4m3_encode(float(blk[i]) * 2.0 ** (-e))
