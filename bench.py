@@ -267,12 +267,12 @@ def main():
 
 
 # kernel-name fragments of the library's kernels, and what each one is
-KERNELS = (("copy_kernel", "copy"), ("dim0_kernel", "dim0_kernel"),
-           ("dim0t_kernel", "dim0t_kernel"),
-           ("dim0_epoch_bump_kernel", "dim0_epoch_bump_kernel"),
-           ("dim1_kernel", "dim1_kernel"), ("mx_dequant_kernel", "mx_dequant_kernel"),
-           ("mx_dim1_kernel", "mx_dim1_kernel"),
-           ("mx_kernel", "mx_kernel"))
+# matched as substrings of the demangled names, first match wins: the more
+# specific names come first
+KERNELS = (("copy_kernel", "copy"), ("mx_dim1_kernel", "mx_dim1_kernel"),
+           ("mx_dequant_kernel", "mx_dequant_kernel"), ("mx_kernel", "mx_kernel"),
+           ("dim0_epoch_bump_kernel", "dim0_epoch_bump_kernel"), ("dim0t_kernel", "dim0t_kernel"),
+           ("dim0_kernel", "dim0_kernel"), ("dim1_kernel", "dim1_kernel"))
 COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -342,8 +342,8 @@ def counter_run(torch, mgs, wl, dev, reps):
     the cache-evicting read between launches, so a counter collector sees
     one dispatch per launch: the 256 MiB copy kernel (known traffic,
     268435456 B read + written), dim0 on T (16640, 8192) G=64, dim1 on T^T
-    G=64, the MX cast on (131072, 5120) FLOOR and RCEIL, and the transposed
-    dim0 on T G=64."""
+    G=64, the MX cast on (131072, 5120) FLOOR and RCEIL, the transposed dim0
+    on T G=64, the MX dim1 cast and the MX dequantisation at the MX shape."""
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -359,12 +359,16 @@ def counter_run(torch, mgs, wl, dev, reps):
     q1, s1 = mgs.mgs_quant_groups_dim1(x1, off)
     q5, s5 = mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR)
     qt, st = mgs.mgs_quant_groups_dim0_t(x0, off)
+    qd1, sd1 = mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR)
+    yd = mgs.mgs_mx_dequant_dim0(q5, s5)
     runs = [lambda: mgs.mgs_copy(src, dst),
             lambda: mgs.mgs_quant_groups_dim0(x0, off, q=q0, scales=s0),
             lambda: mgs.mgs_quant_groups_dim1(x1, off, q=q1, scales=s1),
             lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR, q=q5, scales=s5),
             lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q5, scales=s5),
-            lambda: mgs.mgs_quant_groups_dim0_t(x0, off, q_t=qt, scales_t=st)]
+            lambda: mgs.mgs_quant_groups_dim0_t(x0, off, q_t=qt, scales_t=st),
+            lambda: mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR, q_t=qd1, scales_t=sd1),
+            lambda: mgs.mgs_mx_dequant_dim0(q5, s5, y=yd)]
     for fn in runs:
         for _ in range(reps):
             flush.max()
