@@ -135,6 +135,37 @@ __device__ __forceinline__ uint2 cast8(uint4 v, float s) {
     return cast8(v, s, s, s, s, s, s, s, s);
 }
 
+// Four binary32 values of magnitude below 464 to E4M3 bytes, with no clamp:
+// the hardware conversion rounds to nearest even and gives 0x7E / 0xFE for
+// every magnitude in [448, 464), the same bytes as clamping first. `spare`
+// is any dead register: the first conversion keeps its high half, which the
+// second one overwrites, so no zero has to be moved in.
+__device__ __forceinline__ uint32_t e4m3x4_below464(float a, float b, float c, float d,
+                                                    uint32_t spare) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)spare, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// The per-group cast q = E4M3(fl32(x * s)) of eight bf16, for scales
+// s = fl32(448 / max(amax, EPS)) (or that rounded down to a power of two)
+// with every |x| <= amax of its slice. Then |fl32(x * s)| < 464, so the clamp
+// can be left out: with u = 2^-24, s <= (448 / max(amax, EPS)) (1 + u), hence
+// |x * s| <= 448 (1 + u) and its binary32 rounding is at most 448 (1 + 2u).
+__device__ __forceinline__ uint2 cast8_group(uint4 v, float s0, float s1, float s2, float s3,
+                                             float s4, float s5, float s6, float s7) {
+    uint2 r;
+    r.x = e4m3x4_below464(bf16_lo(v.x) * s0, bf16_hi(v.x) * s1, bf16_lo(v.y) * s2,
+                          bf16_hi(v.y) * s3, v.x);
+    r.y = e4m3x4_below464(bf16_lo(v.z) * s4, bf16_hi(v.z) * s5, bf16_lo(v.w) * s6,
+                          bf16_hi(v.w) * s7, v.z);
+    return r;
+}
+
+__device__ __forceinline__ uint2 cast8_group(uint4 v, float s) {
+    return cast8_group(v, s, s, s, s, s, s, s, s);
+}
+
 // ---- wave primitives ---------------------------------------------------------
 
 // Inclusive prefix max over the 64 lanes of a wave, for non-negative values

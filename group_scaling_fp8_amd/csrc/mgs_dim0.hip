@@ -276,6 +276,7 @@ __device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red)
 struct TileGeom {
     int tpr, tx, ty, rps, col;
     bool col_ok;
+    bool full_width;    // every lane's columns lie inside K (uniform)
 };
 
 __device__ __forceinline__ TileGeom tile_geom(const Tile& t, int K) {
@@ -286,6 +287,7 @@ __device__ __forceinline__ TileGeom tile_geom(const Tile& t, int K) {
     q.rps = kThreads >> t.lt;
     q.col = t.strip * (q.tpr * 8) + q.tx * 8;
     q.col_ok = q.col < K;
+    q.full_width = (t.strip + 1) * (q.tpr * 8) <= K;
     return q;
 }
 
@@ -299,16 +301,26 @@ __device__ __forceinline__ int slab_row(int s, int rps, int ty) {
 }
 
 // Loads rows [r0, r0 + nrows) of this lane's 8 columns into registers.
+// A lane's rows sit at slab_row(s, rps, 0) plus a fixed lane offset, so the
+// addresses are one lane base plus a uniform step per slab; slabs whose rows
+// all exist for every lane of a full-width strip skip the per-lane checks.
 template <bool kQuad>
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t K, int r0, int nrows,
                                           const TileGeom& q, uint4 (&v)[kSlabs]) {
+    const int lane_row = slab_row<kQuad>(0, q.rps, q.ty);
+    const int last_lane_row = slab_row<kQuad>(0, q.rps, q.rps - 1);
+    const uint16_t* p = x + (int64_t)(r0 + lane_row) * K + q.col;
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
         v[s] = make_uint4(0u, 0u, 0u, 0u);
-        if (slab_row<kQuad>(s, q.rps, 0) < nrows) {
-            const int rr = slab_row<kQuad>(s, q.rps, q.ty);
-            if (rr < nrows && q.col_ok) v[s] = load_stream(x + (int64_t)(r0 + rr) * K + q.col);
+        const int r_s = slab_row<kQuad>(s, q.rps, 0);
+        if (r_s + last_lane_row < nrows && q.full_width) {
+            v[s] = load_stream(p);
+        } else if (r_s < nrows) {
+            if (r_s + lane_row < nrows && q.col_ok) v[s] = load_stream(p);
         }
+        if (s + 1 < kSlabs)
+            p += (int64_t)(slab_row<kQuad>(s + 1, q.rps, 0) - r_s) * K;
     }
 }
 
@@ -471,14 +483,15 @@ __device__ __forceinline__ void dim0_body(
                     dst[0] = make_float4(s0, s1, s2, s3);
                     dst[1] = make_float4(s4, s5, s6, s7);
                 }
+                // one lane base, advanced by a uniform step of rps rows
+                uint8_t* qb = q + (int64_t)(t.r0 + geo.ty) * K + geo.col;
+                const int64_t step = (int64_t)geo.rps * K;
 #pragma unroll
                 for (int s = 0; s < kSlabs; ++s) {
-                    if (s * geo.rps < nrows) {
-                        const int rr = s * geo.rps + geo.ty;
-                        if (rr < nrows)
-                            store_stream(q + (int64_t)(t.r0 + rr) * K + geo.col,
-                                         cast8(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
-                    }
+                    const int r_s = s * geo.rps;
+                    if (r_s < nrows && r_s + geo.ty < nrows)
+                        store_stream(qb, cast8_group(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
+                    qb += step;
                 }
             }
         } else {
@@ -511,10 +524,10 @@ __device__ __forceinline__ void dim0_body(
                     if ((qd >= 3) != (ph == 1)) continue;
                     const int row = 4 * (qd * geo.rps + geo.ty);
                     if (row < nrows && geo.col_ok) {
-                        const uint2 b0 = cast8(v[4 * qd + 0], s0, s1, s2, s3, s4, s5, s6, s7);
-                        const uint2 b1 = cast8(v[4 * qd + 1], s0, s1, s2, s3, s4, s5, s6, s7);
-                        const uint2 b2 = cast8(v[4 * qd + 2], s0, s1, s2, s3, s4, s5, s6, s7);
-                        const uint2 b3 = cast8(v[4 * qd + 3], s0, s1, s2, s3, s4, s5, s6, s7);
+                        const uint2 b0 = cast8_group(v[4 * qd + 0], s0, s1, s2, s3, s4, s5, s6, s7);
+                        const uint2 b1 = cast8_group(v[4 * qd + 1], s0, s1, s2, s3, s4, s5, s6, s7);
+                        const uint2 b2 = cast8_group(v[4 * qd + 2], s0, s1, s2, s3, s4, s5, s6, s7);
+                        const uint2 b3 = cast8_group(v[4 * qd + 3], s0, s1, s2, s3, s4, s5, s6, s7);
                         uint32_t lo[4], hi[4];
                         transpose4x4(b0.x, b1.x, b2.x, b3.x, lo);
                         transpose4x4(b0.y, b1.y, b2.y, b3.y, hi);

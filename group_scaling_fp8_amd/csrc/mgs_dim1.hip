@@ -124,7 +124,7 @@ __global__ __launch_bounds__(1024) void dim1_kernel(
             if (gid != kNoGroup) {
                 const int vi = cc * chunk_vecs + threadIdx.x + NT * j;
                 // a plain store: measured faster here than a nontemporal one
-                *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = cast8(v[j], s_scale[gid]);
+                *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = cast8_group(v[j], s_scale[gid]);
             }
         }
     };

@@ -291,6 +291,61 @@ def test_every_finite_bf16_through_dim1():
         check_dim1(rows, np.array([16], np.int32), False, "bf16 sweep %d" % variant)
 
 
+def bf16_sweep_columns(variant):
+    """(16, N) bf16 with column j = [x_j, anchor_j, 0, ...] over every finite
+    bf16 x_j (N padded to a multiple of 8 with zero columns), and how many of
+    its products fl32(x * s) exceed 448 in magnitude (those the grouped
+    kernels' cast reaches without a clamp)."""
+    b = np.arange(0x10000, dtype=np.uint32)
+    xs = b[(b & 0x7F80) != 0x7F80].astype(np.uint16)
+    mags = xs & 0x7FFF
+    if variant == 0:
+        anchor = mags.copy()
+    elif variant == 1:
+        anchor = (((mags >> 7) + 1) << 7).astype(np.uint16)
+    else:
+        anchor = ((((mags >> 7) + 1) << 7) | 0x60).astype(np.uint16)
+    anchor = np.where(mags == 0, 0x3F80, anchor)
+    ok = (anchor & 0x7F80) != 0x7F80
+    n = int(ok.sum())
+    N = (n + 7) // 8 * 8
+    x = np.zeros((16, N), np.uint16)
+    x[0, :n] = xs[ok]
+    x[1, :n] = anchor[ok]
+    f32 = lambda u: (u.astype(np.uint32) << 16).view(np.float32)
+    s = np.float32(448.0) / np.maximum(f32(anchor[ok]), np.float32(1e-12))
+    above = int(np.count_nonzero(np.abs(f32(xs[ok]) * s) > np.float32(448.0)))
+    return x, above
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_every_finite_bf16_through_dim0(variant):
+    """The dim0 kernel's cast on every finite bf16 value, with the scale of its
+    column fixed by an anchor; the anchor = |x| sweep reaches binary32
+    products just above 448, which must give 0x7E / 0xFE."""
+    x, above = bf16_sweep_columns(variant)
+    if variant == 0:
+        assert above > 1000
+    off = np.array([16], np.int32)
+    for pow2 in (False, True):
+        check_dim0(x, off, pow2, "dim0 bf16 sweep %d pow2=%s" % (variant, pow2))
+
+
+def test_every_finite_bf16_through_dim0_t():
+    x, above = bf16_sweep_columns(0)
+    assert above > 1000
+    off = np.array([16], np.int32)
+    M, K = x.shape
+    gq, gs = Guarded((K, M), torch.uint8), Guarded((K, 1), torch.float32)
+    mgs.mgs_quant_groups_dim0_t(to_dev(x), to_dev(off), False, q_t=gq.view, scales_t=gs.view)
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    rq, rs = oracle.quant_groups_dim0_t(x, off, False)
+    assert_same_bytes(gs.numpy(), rs, "dim0_t bf16 sweep scales_t")
+    assert_same_bytes(gq.numpy(), rq, "dim0_t bf16 sweep q_t")
+
+
 # ------------------------------------------------- identities, determinism
 
 
