@@ -136,13 +136,14 @@ namespace mgs {
 struct DeviceInfo {
     long long spin_ticks;   // 20 ms of the device wall clock
     int team_max;           // min(kDim0MaxTeam, CU count)
+    int cus;                // compute units
 };
 
 DeviceInfo device_info() {
     static std::mutex mu;
     static std::map<int, DeviceInfo> per_device;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DeviceInfo{2000000, 1};
+    if (hipGetDevice(&dev) != hipSuccess) return DeviceInfo{2000000, 1, 1};
     std::lock_guard<std::mutex> lock(mu);
     auto it = per_device.find(dev);
     if (it != per_device.end()) return it->second;
@@ -151,7 +152,7 @@ DeviceInfo device_info() {
         khz = 100000;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 1;
-    DeviceInfo d{20LL * khz, cus < kDim0MaxTeam ? cus : kDim0MaxTeam};
+    DeviceInfo d{20LL * khz, cus < kDim0MaxTeam ? cus : kDim0MaxTeam, cus};
     per_device[dev] = d;
     return d;
 }
@@ -195,7 +196,8 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
     }
     const mgs::DeviceInfo dinfo = mgs::device_info();
     const int team_max = mgs::dim0_team_max(dinfo);
-    if (mgs::dim0_tile_bound(M, K, n_groups, team_max) >= INT32_MAX)
+    const int lt_cap = mgs::dim0_lt_cap(M, K, n_groups, team_max, dinfo.cus);
+    if (mgs::dim0_tile_bound(M, K, n_groups, team_max, lt_cap) >= INT32_MAX)
         return MGS_ERR_UNSUPPORTED;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);
@@ -217,7 +219,7 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
     return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, (int)K, offsets,
                                        n_groups, (int)uniform_rows,
                                        (flags & MGS_FLAG_POW2_SCALE) != 0, transposed,
-                                       static_cast<uint8_t*>(q), scales, team_max, ws, gen,
+                                       static_cast<uint8_t*>(q), scales, team_max, lt_cap, ws, gen,
                                        mgs::dim0_spin_ticks(dinfo), s));
 }
 

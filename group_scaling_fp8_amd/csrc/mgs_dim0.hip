@@ -600,18 +600,15 @@ __global__ void dim0_epoch_bump_kernel(uint32_t* __restrict__ ws_epoch) {
 }
 
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
-                       bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, void* ws,
-                       uint32_t gen, long long spin_ticks, hipStream_t stream) {
-    const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max);
+                       bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
+                       void* ws, uint32_t gen, long long spin_ticks, hipStream_t stream) {
+    const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max, lt_cap);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
     const int64_t grid = n_tiles < kDim0MaxGrid ? n_tiles : kDim0MaxGrid;
     const Dim0Workspace w = dim0_workspace(M, K);
     char* base = static_cast<char*>(ws);
     const uint32_t* ws_epoch = base ? reinterpret_cast<const uint32_t*>(base + w.epoch_off) : nullptr;
     uint64_t* ws_max = base ? reinterpret_cast<uint64_t*>(base + w.max_off) : nullptr;
-    // strips never wider than K needs: the smallest lt >= 3 with 8 << lt >= K
-    int lt_cap = 3;
-    while (lt_cap < 7 && (int64_t(8) << lt_cap) < K) ++lt_cap;
     // a group can need column-maximum tiles only if M rows make more chunks
     // than a team may have
     const int maybe_c = (int64_t)M > (int64_t)kRowsW128 * team_max ? 1 : 0;

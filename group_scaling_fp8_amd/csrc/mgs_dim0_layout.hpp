@@ -31,12 +31,16 @@ inline int64_t dim0_chunk_bound(int64_t M) {
 }
 
 // Tiles of one group of R rows (the rule of the kernel's tile search):
-// n(w) = ceil(K / w) strips of width w = 1024 columns for R <= 80, 512 up to
-// 160, 256 up to 320 and 128 up to 640. A taller group has c = ceil(R / 640)
-// chunks on n(128) strips: c * n(128) tiles as a team (c <= team_max), else
-// 2 * c * n(128).
-inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max) {
-    auto n = [K](int64_t w) { return (K + w - 1) / w; };
+// n(w) = ceil(K / w') strips of width w' = min(w, 8 << max_lt) with
+// w = 1024 columns for R <= 80, 512 up to 160, 256 up to 320 and 128 up to
+// 640. A taller group has c = ceil(R / 640) chunks on n(128) strips:
+// c * n(128) tiles as a team (c <= team_max), else 2 * c * n(128).
+inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max, int max_lt = 7) {
+    const int64_t wmax = int64_t(8) << max_lt;
+    auto n = [K, wmax](int64_t w) {
+        const int64_t wc = w < wmax ? w : wmax;
+        return (K + wc - 1) / wc;
+    };
     if (R <= 80) return n(1024);
     if (R <= 160) return n(512);
     if (R <= 320) return n(256);
@@ -56,13 +60,14 @@ inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max) {
 // tiles <= G * tiles(M) as well; the bound is the smaller of the two.
 // Team steps: rho falls with the chunk count c unless K <= 128, so all of
 // them (2 <= c <= team_max <= 128) are scanned; past team_max only the
-// first.
-inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max) {
-    const int64_t base = dim0_group_tiles(0, K, team_max);
+// first. A strip-width cap (max_lt) only merges steps, so the same rows
+// bound it.
+inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max, int max_lt = 7) {
+    const int64_t base = dim0_group_tiles(0, K, team_max, max_lt);
     int64_t extra = 0;
     auto step = [&](int64_t first_rows) {
         if (first_rows > M) return;
-        const int64_t num = dim0_group_tiles(first_rows, K, team_max) - base;
+        const int64_t num = dim0_group_tiles(first_rows, K, team_max, max_lt) - base;
         const int64_t e = M * num / first_rows;
         if (e > extra) extra = e;
     };
@@ -73,8 +78,23 @@ inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max
     const int64_t last = team_max + 1 > 2 ? team_max + 1 : 2;
     for (int64_t c = 2; c <= last; ++c) step(kDim0ChunkRows * (c - 1) + 1);
     const int64_t spread = G * base + extra;
-    const int64_t one = G * dim0_group_tiles(M, K, team_max);
+    const int64_t one = G * dim0_group_tiles(M, K, team_max, max_lt);
     return spread < one ? spread : one;
+}
+
+// Widest strips the launch may use (log2 of 8-column units per strip, 3..7).
+// Never wider than K needs. A tiny problem also gets narrower strips, down
+// to 64 columns, until G groups of M / G rows would make at least one tile
+// per CU: otherwise a handful of tiles leaves most CUs idle. Only then:
+// strips under 256 bytes of bf16 per row stream poorly, and problems with a
+// few hundred tiles already run faster on the wide ones.
+inline int dim0_lt_cap(int64_t M, int64_t K, int64_t G, int64_t team_max, int64_t cus) {
+    int lt = 3;
+    while (lt < 7 && (int64_t(8) << lt) < K) ++lt;
+    if (G < 1) return lt;
+    const int64_t want = cus;
+    while (lt > 3 && G * dim0_group_tiles(M / G, K, team_max, lt) < want) --lt;
+    return lt;
 }
 
 // dim0 workspace (needed only when M > kDim0TeamRows), 256-byte aligned

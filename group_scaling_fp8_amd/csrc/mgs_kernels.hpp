@@ -15,12 +15,13 @@ namespace mgs {
 // order (for graph replays). spin_ticks bounds a tile's wait for maxima
 // written by other tiles, in device wall-clock ticks; past it the tile
 // computes them itself. A negative value skips the wait.
+// lt_cap: the widest strips allowed, 8 << lt_cap columns (dim0_lt_cap).
 // uniform_rows >= 0: G equal groups of that many rows and no offsets array
 // (off unused); -1: group ends from off. transposed: q is (K, M) and scales (K, G) (dim0_t); M and the
 // group ends must then be multiples of 16 (ends are rounded down to them).
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
-                       bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, void* ws,
-                       uint32_t gen, long long spin_ticks, hipStream_t stream);
+                       bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
+                       void* ws, uint32_t gen, long long spin_ticks, hipStream_t stream);
 
 hipError_t launch_dim0_epoch_bump(void* ws, hipStream_t stream);
 
