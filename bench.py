@@ -411,7 +411,7 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
     rows = []
 
-    def add(name, kind, x, off, bytes_, fn_maker):
+    def add(name, kind, x, off, bytes_, fn_maker, elems=None):
         fn = fn_maker()
         fn()
         torch.cuda.synchronize()
@@ -422,6 +422,10 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
                      "pct_hbm_peak": round(100 * bytes_ / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
                      "us_steady": round(sty, 2),
                      "steady_GBps": round(bytes_ / (sty * 1e-6) / 1e9, 1)})
+        if elems is not None:
+            # the rowwise page's bytes convention: bf16 input counted twice
+            # (2R + 1W + scales), for a like-for-like look at its table
+            rows[-1]["page_convention_GBps"] = round((bytes_ + 2 * elems) / (med * 1e-6) / 1e9, 1)
         log("  %-44s %9.2f us  %7.1f GB/s   back-to-back %9.2f us  %7.1f GB/s"
             % (name, med, rows[-1]["algorithmic_GBps"], sty, rows[-1]["steady_GBps"]))
 
@@ -444,7 +448,7 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
     for w in [wl.c1_dim0_small(), wl.c2_dim0_pow2(), wl.c3_dim0_large(),
               wl.c6_dim0_target(64, T)] + tall + [wl.c4_dim1(1, T), wl.c4_dim1(16, T),
                                                   wl.c4_dim1(64, T)]:
-        add(w.name, w.kind, w.x, w.offsets, w.algorithmic_bytes(), grouped(w))
+        add(w.name, w.kind, w.x, w.offsets, w.algorithmic_bytes(), grouped(w), elems=w.x.size)
         del w
     # the fused quantize + transpose of T: (8192, 16640) e4m3 and (8192, 64)
     # scales, the same bytes as dim0 at this shape

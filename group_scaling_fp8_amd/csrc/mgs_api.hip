@@ -262,7 +262,7 @@ int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* of
     }
     return hip_status(mgs::launch_dim1(static_cast<const uint16_t*>(x), M, (int)K, offsets,
                                        n_groups, (flags & MGS_FLAG_POW2_SCALE) != 0,
-                                       static_cast<uint8_t*>(q), scales,
+                                       static_cast<uint8_t*>(q), scales, mgs::device_info().cus,
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -23,8 +23,9 @@
 //   * class A, R <= 640 rows: one tile per strip. tpr is the widest power of
 //     two in [16, 128] whose tile fits (short groups get strips up to 1024
 //     columns). Load -> column amax -> scale -> cast from registers -> store.
-//     No strip is narrower than 128 columns unless K is: rows of 128 bytes
-//     stream far worse than rows of 256.
+//     No strip is narrower than 128 columns unless K is, or the launch would
+//     otherwise have fewer tiles than CUs (lt_cap, from dim0_lt_cap): rows of
+//     128 bytes stream far worse than rows of 256.
 //   * class T, R > 640 rows and at most team_max chunks: the group is cut
 //     into c = ceil(R / 640) chunks on 128-column strips, and the c tiles of
 //     a strip are consecutive in the grid (a team). Each loads its chunk,

@@ -25,8 +25,9 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
 
 hipError_t launch_dim0_epoch_bump(void* ws, hipStream_t stream);
 
+// cus: compute units of the device; the grid is the workgroups that fit at once.
 hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,
-                       uint8_t* q, float* scales, hipStream_t stream);
+                       uint8_t* q, float* scales, int cus, hipStream_t stream);
 
 hipError_t launch_mx(const uint16_t* x, int64_t n_elems, bool rceil, uint8_t* q, uint8_t* scales,
                      hipStream_t stream);
