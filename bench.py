@@ -439,9 +439,9 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
     log("per-config kernel times (cache flushed before each launch; then back-to-back launches):")
     M = T.shape[0]
     tall = [
-        # every row in one group: 26 chunks of 640 rows (column maxima through the workspace)
+        # every row in one group: 19 chunks of up to 896 rows (column maxima through the workspace)
         wl.Workload("dim0 (16640,8192) G=1", "dim0", T, np.array([M], dtype=np.int32)),
-        # eight groups of 2080 rows: teams of four 520-row chunks
+        # eight groups of 2080 rows: teams of three 694-row chunks
         wl.Workload("dim0 (16640,8192) G=8 even", "dim0", T,
                     np.arange(1, 9, dtype=np.int32) * (M // 8)),
     ]
@@ -460,7 +460,7 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
         lambda: (lambda: mgs.mgs_quant_groups_dim0_t(xt6, ot6, q_t=qt6, scales_t=st6)))
     del w, xt6, ot6, qt6, st6
     # per-expert scaling of a 3D weight along dim 1: 16 experts of (5120, 8192),
-    # each expert a 5120-row group cut into 8-chunk teams (seeded on the GPU)
+    # each expert a 5120-row group cut into 6-chunk teams (seeded on the GPU)
     E, D1, D2 = 16, 5120, 8192
     gen = torch.Generator(device=dev).manual_seed(7)
     w3 = (torch.randn((E, D1, D2), generator=gen, device=dev) * 0.02).to(torch.bfloat16)

@@ -196,8 +196,9 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
     }
     const mgs::DeviceInfo dinfo = mgs::device_info();
     const int team_max = mgs::dim0_team_max(dinfo);
-    const int lt_cap = mgs::dim0_lt_cap(M, K, n_groups, team_max, dinfo.cus);
-    if (mgs::dim0_tile_bound(M, K, n_groups, team_max, lt_cap) >= INT32_MAX)
+    const int64_t chunk_rows = transposed ? mgs::kDim0ChunkRowsT : mgs::kDim0ChunkRows;
+    const int lt_cap = mgs::dim0_lt_cap(M, K, n_groups, team_max, dinfo.cus, chunk_rows);
+    if (mgs::dim0_tile_bound(M, K, n_groups, team_max, lt_cap, chunk_rows) >= INT32_MAX)
         return MGS_ERR_UNSUPPORTED;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);

@@ -49,6 +49,10 @@ __device__ __forceinline__ uint32_t mag_fold(uint32_t w) {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Cache-policy argument of __builtin_amdgcn_global_load_lds for a
+// nontemporal load (the nt bit, as load_stream's loads carry).
+constexpr int kLoadNontemporal = 2;
+
 // 16 bytes of input read once: a nontemporal load, so the streamed input does
 // not push reusable lines out of L2 and the Infinity Cache.
 __device__ __forceinline__ uint4 load_stream(const void* p) {

@@ -17,17 +17,23 @@
 // below at 0, so any offsets array gives in-range rows.
 //
 // A 512-thread workgroup holds up to kSlabs 16-byte vectors per thread in
-// registers (160 KiB of bf16), and every byte of x is loaded once into them.
-// A tile is rows of one group times a strip of 8 * tpr columns, tpr lanes
-// per row:
-//   * class A, R <= 640 rows: one tile per strip. tpr is the widest power of
+// registers (160 KiB of bf16) and, in the plain kernel, kLdsSlabs more in LDS
+// (64 KiB, loaded straight from global memory with global_load_lds), and
+// every byte of x is loaded once into them. One CU alone streams only a few
+// tens of GB/s, so HBM is full only while every CU has loads in flight;
+// holding 224 KiB per tile lets a group of up to 896 rows (C below; 640 in
+// the transposed kernel, whose LDS holds its output stage) be one tile and
+// gives 449-896-row groups strips of 256 and 128 columns instead of chunk
+// teams. A tile is rows of one group times a strip of 8 * tpr columns, tpr
+// lanes per row:
+//   * class A, R <= C rows: one tile per strip. tpr is the widest power of
 //     two in [16, 128] whose tile fits (short groups get strips up to 1024
 //     columns). Load -> column amax -> scale -> cast from registers -> store.
 //     No strip is narrower than 128 columns unless K is, or the launch would
 //     otherwise have fewer tiles than CUs (lt_cap, from dim0_lt_cap): rows of
 //     128 bytes stream far worse than rows of 256.
-//   * class T, R > 640 rows and at most team_max chunks: the group is cut
-//     into c = ceil(R / 640) chunks on 128-column strips, and the c tiles of
+//   * class T, R > C rows and at most team_max chunks: the group is cut
+//     into c = ceil(R / C) chunks on 128-column strips, and the c tiles of
 //     a strip are consecutive in the grid (a team). Each loads its chunk,
 //     writes the chunk's column maxima to a workspace, waits for the maxima
 //     of the other chunks of its strip, and casts its chunk from registers.
@@ -56,13 +62,15 @@ namespace mgs {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kSlabs = kDim0Slabs;                    // vectors per thread
-constexpr int kCap = kThreads * kSlabs;               // vectors per tile
-constexpr int kRowsW128 = kCap / 16;                  // 640 rows at 128 columns
-static_assert(kRowsW128 == kDim0ChunkRows, "chunk size mismatch");
-static_assert(kRowsW128 == kDim0TeamRows, "chunking threshold mismatch");
-static_assert((kCap >> 7) == 80 && (kCap >> 6) == 160 && (kCap >> 5) == 320,
-              "strip steps assumed by dim0_group_tiles");
+constexpr int kSlabs = kDim0Slabs;                    // vectors per thread in registers
+constexpr int kLdsSlabs = kDim0LdsSlabs;              // more per thread in LDS (dim0 only)
+// Rows of a full 128-column tile (16 lanes per row, 32 rows per slab): the
+// chunk size, and 8x / 4x / 2x the rows of the 1024 / 512 / 256-column steps.
+template <bool kT>
+constexpr int rows_w128() { return kThreads * (kSlabs + (kT ? 0 : kLdsSlabs)) / 16; }
+static_assert(rows_w128<false>() == kDim0ChunkRows, "dim0 chunk size mismatch");
+static_assert(rows_w128<true>() == kDim0ChunkRowsT, "dim0_t chunk size mismatch");
+static_assert(kDim0ChunkRows % 8 == 0 && kDim0ChunkRowsT % 8 == 0, "strip steps");
 constexpr int kStreamSlabs = 4;                       // rows in flight per lane for streamed rows
 
 enum { kClassA = 0, kClassT = 1, kClassC = 2 };
@@ -87,6 +95,7 @@ struct GroupInfo {
     int chunks;     // workspace rows (classes T, C)
 };
 
+template <int kRows>
 __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, int K, int team_max,
                                                 int lt_cap) {
     GroupInfo gi;
@@ -94,12 +103,12 @@ __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, 
     gi.R = end - start;
     const int R = gi.R;
     gi.nc = 1;
-    if (R > kRowsW128) {
+    if (R > kRows) {
         gi.lt = 4;
-        gi.nc = (R + kRowsW128 - 1) / kRowsW128;
+        gi.nc = (R + kRows - 1) / kRows;
         gi.cls = gi.nc <= team_max ? kClassT : kClassC;
     } else {
-        gi.lt = R <= (kCap >> 7) ? 7 : (R <= (kCap >> 6) ? 6 : (R <= (kCap >> 5) ? 5 : 4));
+        gi.lt = R <= kRows / 8 ? 7 : (R <= kRows / 4 ? 6 : (R <= kRows / 2 ? 5 : 4));
         gi.cls = kClassA;
     }
     // no strip wider than needed to cover K
@@ -164,6 +173,7 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
 // by every wave of the workgroup; all lanes return the same tile.
 // Group ends come from off (uniform_rows < 0), or are (g + 1) * uniform_rows
 // (equal groups, e.g. the experts of a 3D weight, with no offsets array).
+template <int kRows>
 __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
                           int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -180,7 +190,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         // the previous lane's end (wave_shr:1); lane 0 keeps carry_end
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
-        const GroupInfo gi = group_info(start, end, g < G, K, team_max, lt_cap);
+        const GroupInfo gi = group_info<kRows>(start, end, g < G, K, team_max, lt_cap);
         const int incl_x = maybe_c ? wave_prefix_sum_dpp(gi.cnt_x) + carry_x : 0;
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
@@ -221,7 +231,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
             -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
-        const GroupInfo gi = group_info(start, end, g < G, K, team_max, lt_cap);
+        const GroupInfo gi = group_info<kRows>(start, end, g < G, K, team_max, lt_cap);
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
         const uint64_t hm = __ballot(gi.cnt_m > 0 && target >= incl_m - gi.cnt_m && target < incl_m);
@@ -325,6 +335,32 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Plain layout only: slabs kSlabs .. kSlabs + kLdsSlabs - 1 (rows
+// (kSlabs + e) * rps + ty) go straight from global memory into LDS
+// (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the wave's
+// LDS base + 16 i), so thread t owns ext[e * kThreads + t]. Lanes whose row
+// or columns do not exist load nothing, and ext_slab masks them.
+__device__ __forceinline__ void load_tile_ext(const uint16_t* __restrict__ x, int64_t K, int r0,
+                                              int nrows, const TileGeom& q, uint4* ext) {
+    const int wave = threadIdx.x / kWave;
+    const uint16_t* p = x + (int64_t)(r0 + kSlabs * q.rps + q.ty) * K + q.col;
+#pragma unroll
+    for (int e = 0; e < kLdsSlabs; ++e) {
+        const int r_s = (kSlabs + e) * q.rps;
+        if (r_s + q.ty < nrows && q.col_ok)
+            __builtin_amdgcn_global_load_lds(p, (lds_void*)(ext + e * kThreads + wave * kWave), 16, 0,
+                                             kLoadNontemporal);
+        p += (int64_t)q.rps * K;
+    }
+}
+
+__device__ __forceinline__ uint4 ext_slab(const uint4* ext, int e, int nrows, const TileGeom& q) {
+    if ((kSlabs + e) * q.rps + q.ty < nrows && q.col_ok) return ext[e * kThreads + threadIdx.x];
+    return make_uint4(0u, 0u, 0u, 0u);
+}
+
 // Running column amax of rows [r0, r0 + nrows) of this lane's columns,
 // streamed through a few registers.
 __device__ __forceinline__ void stream_amax(const uint16_t* __restrict__ x, int64_t K, int r0, int nrows,
@@ -417,13 +453,14 @@ __device__ __forceinline__ void dim0_body(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks, int uniform_rows, uint4* red, uint32_t* stage) {
+        uint32_t gen_arg, long long spin_ticks, int uniform_rows, uint4* red, uint32_t* stage,
+        uint4* ext) {
     constexpr int kRowAlign = kT ? 16 : 1;
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign, uniform_rows,
-                                 (int)item);
+        const Tile t = find_tile<rows_w128<kT>()>(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign,
+                                                   uniform_rows, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);
         const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
@@ -443,10 +480,21 @@ __device__ __forceinline__ void dim0_body(
 
         uint4 v[kSlabs];
         load_tile<kT>(x, K, t.r0, nrows, geo, v);
+        // rows past the registers' (plain layout): into LDS
+        const bool use_ext = !kT && kSlabs * geo.rps < nrows;
+        if (use_ext) load_tile_ext(x, K, t.r0, nrows, geo, ext);
         if (t.cls != kClassC || t.maxima) {
 #pragma unroll
             for (int s = 0; s < kSlabs; ++s)
                 if (slab_row<kT>(s, geo.rps, 0) < nrows) max4(m, v[s]);
+        }
+        if (use_ext) {
+            // every load of this thread, the LDS ones included, has landed
+            __builtin_amdgcn_s_waitcnt(0);
+            if (t.cls != kClassC || t.maxima) {
+#pragma unroll
+                for (int e = 0; e < kLdsSlabs; ++e) max4(m, ext_slab(ext, e, nrows, geo));
+            }
         }
 
         if (t.maxima) {
@@ -493,6 +541,15 @@ __device__ __forceinline__ void dim0_body(
                     if (r_s < nrows && r_s + geo.ty < nrows)
                         store_stream(qb, cast8_group(v[s], s0, s1, s2, s3, s4, s5, s6, s7));
                     qb += step;
+                }
+                if (use_ext) {
+#pragma unroll
+                    for (int e = 0; e < kLdsSlabs; ++e) {
+                        if ((kSlabs + e) * geo.rps + geo.ty < nrows)
+                            store_stream(qb, cast8_group(ext[e * kThreads + threadIdx.x], s0, s1, s2, s3,
+                                                         s4, s5, s6, s7));
+                        qb += step;
+                    }
                 }
             }
         } else {
@@ -574,8 +631,9 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
         uint32_t gen_arg, long long spin_ticks, int uniform_rows) {
     __shared__ uint4 red[kThreads];
+    __shared__ uint4 ext[kLdsSlabs * kThreads];     // 64 KiB: the tile's rows past the registers
     dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
-                     ws_max, gen_arg, spin_ticks, uniform_rows, red, nullptr);
+                     ws_max, gen_arg, spin_ticks, uniform_rows, red, nullptr, ext);
 }
 
 // The same per-group scaling with transposed outputs: qT (K, M), scalesT (K, G).
@@ -587,7 +645,8 @@ __global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
     __shared__ uint4 red[kThreads];
     __shared__ uint4 stage[kStageWords / 4];
     dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
-                    ws_max, gen_arg, spin_ticks, uniform_rows, red, reinterpret_cast<uint32_t*>(stage));
+                    ws_max, gen_arg, spin_ticks, uniform_rows, red, reinterpret_cast<uint32_t*>(stage),
+                    nullptr);
 }
 
 // Advances the epoch word by one, keeping its top bit set so that epochs
@@ -603,7 +662,8 @@ __global__ void dim0_epoch_bump_kernel(uint32_t* __restrict__ ws_epoch) {
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
                        bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
                        void* ws, uint32_t gen, long long spin_ticks, hipStream_t stream) {
-    const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max, lt_cap);
+    const int64_t chunk_rows = transposed ? kDim0ChunkRowsT : kDim0ChunkRows;
+    const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max, lt_cap, chunk_rows);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
     const int64_t grid = n_tiles < kDim0MaxGrid ? n_tiles : kDim0MaxGrid;
     const Dim0Workspace w = dim0_workspace(M, K);
@@ -612,7 +672,7 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
     uint64_t* ws_max = base ? reinterpret_cast<uint64_t*>(base + w.max_off) : nullptr;
     // a group can need column-maximum tiles only if M rows make more chunks
     // than a team may have
-    const int maybe_c = (int64_t)M > (int64_t)kRowsW128 * team_max ? 1 : 0;
+    const int maybe_c = (int64_t)M > chunk_rows * team_max ? 1 : 0;
     hipLaunchKernelGGL(transposed ? dim0t_kernel : dim0_kernel, dim3((unsigned)grid), dim3(kThreads),
                        0, stream, x, M, K, off, G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max,
                        lt_cap, maybe_c, ws_epoch, ws_max, gen, spin_ticks, uniform_rows);

@@ -8,44 +8,49 @@
 namespace mgs {
 
 // dim0 tiling: 512-thread workgroups holding kDim0Slabs 16-byte vectors per
-// thread (10240 vectors, 160 KiB of bf16). A group of at most kDim0TeamRows
-// rows is one tile per column strip. A taller group is cut into chunks of at
-// most kDim0ChunkRows rows on 128-column strips: a team of chunk tiles per
-// strip when the chunk count is at most the team limit, else a
+// thread in registers (10240 vectors, 160 KiB of bf16), and in the plain
+// dim0 kernel kDim0LdsSlabs more per thread in LDS (4096 vectors, 64 KiB;
+// the transposed kernel's LDS holds its output stage instead). A group of
+// at most chunk_rows rows (the rows of a full 128-column tile: 896 for dim0,
+// 640 for dim0_t) is one tile per column strip. A taller group is cut into
+// chunks of at most chunk_rows rows on 128-column strips: a team of chunk
+// tiles per strip when the chunk count is at most the team limit, else a
 // column-maximum tile and a casting tile per chunk and strip.
 constexpr int kDim0Slabs = 20;
-constexpr int kDim0TeamRows = 640;
-constexpr int kDim0ChunkRows = 640;
+constexpr int kDim0LdsSlabs = 8;
+constexpr int kDim0ChunkRows = (kDim0Slabs + kDim0LdsSlabs) * 512 / 16;    // 896
+constexpr int kDim0ChunkRowsT = kDim0Slabs * 512 / 16;                     // 640
 // Upper limit on the chunk count of a team (the library also keeps it at
 // most the CU count, so that a team fits among the resident workgroups).
 constexpr int kDim0MaxTeam = 128;
 // Largest dim0 grid launched at once; past it the workgroups loop.
 constexpr int64_t kDim0MaxGrid = int64_t(1) << 22;
 
-// Upper bound on the chunks of all chunked groups: a group of s > 640 rows
-// has ceil(s / 640) <= floor(s / 640) + 1 chunks, and there are at most
-// M / 641 such groups.
-inline int64_t dim0_chunk_bound(int64_t M) {
-    if (M <= kDim0TeamRows) return 0;
-    return M / kDim0ChunkRows + M / (kDim0TeamRows + 1);
+// Upper bound on the chunks of all chunked groups: a group of s > C rows
+// (C = chunk_rows) has ceil(s / C) <= floor(s / C) + 1 chunks, and there are
+// at most M / (C + 1) such groups.
+inline int64_t dim0_chunk_bound(int64_t M, int64_t chunk_rows) {
+    if (M <= chunk_rows) return 0;
+    return M / chunk_rows + M / (chunk_rows + 1);
 }
 
-// Tiles of one group of R rows (the rule of the kernel's tile search):
-// n(w) = ceil(K / w') strips of width w' = min(w, 8 << max_lt) with
-// w = 1024 columns for R <= 80, 512 up to 160, 256 up to 320 and 128 up to
-// 640. A taller group has c = ceil(R / 640) chunks on n(128) strips:
+// Tiles of one group of R rows (the rule of the kernel's tile search), with
+// C = chunk_rows: n(w) = ceil(K / w') strips of width w' = min(w, 8 << max_lt)
+// with w = 1024 columns for R <= C/8, 512 up to C/4, 256 up to C/2 and 128
+// up to C. A taller group has c = ceil(R / C) chunks on n(128) strips:
 // c * n(128) tiles as a team (c <= team_max), else 2 * c * n(128).
-inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max, int max_lt = 7) {
+inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max, int max_lt,
+                                int64_t chunk_rows) {
     const int64_t wmax = int64_t(8) << max_lt;
     auto n = [K, wmax](int64_t w) {
         const int64_t wc = w < wmax ? w : wmax;
         return (K + wc - 1) / wc;
     };
-    if (R <= 80) return n(1024);
-    if (R <= 160) return n(512);
-    if (R <= 320) return n(256);
-    if (R <= 640) return n(128);
-    const int64_t c = (R + kDim0ChunkRows - 1) / kDim0ChunkRows;
+    if (R <= chunk_rows / 8) return n(1024);
+    if (R <= chunk_rows / 4) return n(512);
+    if (R <= chunk_rows / 2) return n(256);
+    if (R <= chunk_rows) return n(128);
+    const int64_t c = (R + chunk_rows - 1) / chunk_rows;
     return (c <= team_max ? 1 : 2) * c * n(128);
 }
 
@@ -62,23 +67,24 @@ inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max, int max_
 // them (2 <= c <= team_max <= 128) are scanned; past team_max only the
 // first. A strip-width cap (max_lt) only merges steps, so the same rows
 // bound it.
-inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max, int max_lt = 7) {
-    const int64_t base = dim0_group_tiles(0, K, team_max, max_lt);
+inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max, int max_lt,
+                               int64_t chunk_rows) {
+    const int64_t base = dim0_group_tiles(0, K, team_max, max_lt, chunk_rows);
     int64_t extra = 0;
     auto step = [&](int64_t first_rows) {
         if (first_rows > M) return;
-        const int64_t num = dim0_group_tiles(first_rows, K, team_max, max_lt) - base;
+        const int64_t num = dim0_group_tiles(first_rows, K, team_max, max_lt, chunk_rows) - base;
         const int64_t e = M * num / first_rows;
         if (e > extra) extra = e;
     };
-    step(81);
-    step(161);
-    step(321);
-    // chunked groups have at least 2 chunks (more than 640 rows)
+    step(chunk_rows / 8 + 1);
+    step(chunk_rows / 4 + 1);
+    step(chunk_rows / 2 + 1);
+    // chunked groups have at least 2 chunks (more than chunk_rows rows)
     const int64_t last = team_max + 1 > 2 ? team_max + 1 : 2;
-    for (int64_t c = 2; c <= last; ++c) step(kDim0ChunkRows * (c - 1) + 1);
+    for (int64_t c = 2; c <= last; ++c) step(chunk_rows * (c - 1) + 1);
     const int64_t spread = G * base + extra;
-    const int64_t one = G * dim0_group_tiles(M, K, team_max, max_lt);
+    const int64_t one = G * dim0_group_tiles(M, K, team_max, max_lt, chunk_rows);
     return spread < one ? spread : one;
 }
 
@@ -88,18 +94,21 @@ inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max
 // per CU: otherwise a handful of tiles leaves most CUs idle. Only then:
 // strips under 256 bytes of bf16 per row stream poorly, and problems with a
 // few hundred tiles already run faster on the wide ones.
-inline int dim0_lt_cap(int64_t M, int64_t K, int64_t G, int64_t team_max, int64_t cus) {
+inline int dim0_lt_cap(int64_t M, int64_t K, int64_t G, int64_t team_max, int64_t cus,
+                       int64_t chunk_rows) {
     int lt = 3;
     while (lt < 7 && (int64_t(8) << lt) < K) ++lt;
     if (G < 1) return lt;
     const int64_t want = cus;
-    while (lt > 3 && G * dim0_group_tiles(M / G, K, team_max, lt) < want) --lt;
+    while (lt > 3 && G * dim0_group_tiles(M / G, K, team_max, lt, chunk_rows) < want) --lt;
     return lt;
 }
 
-// dim0 workspace (needed only when M > kDim0TeamRows), 256-byte aligned
+// dim0 workspace (needed only when M > kDim0ChunkRowsT), 256-byte aligned
 // regions: an epoch word, then the column maxima of every chunk, one 64-bit
 // word per column pair (generation << 32 | two 16-bit magnitude patterns).
+// Sized for the smaller chunks (dim0_t's), so one workspace serves both
+// kernels.
 struct Dim0Workspace {
     int64_t chunks;
     size_t epoch_off, max_off, bytes;
@@ -107,7 +116,7 @@ struct Dim0Workspace {
 
 inline Dim0Workspace dim0_workspace(int64_t M, int64_t K) {
     Dim0Workspace w;
-    w.chunks = dim0_chunk_bound(M);
+    w.chunks = dim0_chunk_bound(M, kDim0ChunkRowsT);
     w.epoch_off = 0;
     w.max_off = 256;
     w.bytes = w.max_off + (size_t)(w.chunks * (K / 2)) * sizeof(uint64_t);

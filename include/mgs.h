@@ -80,8 +80,9 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * Requirements: M >= 0, K >= 0, K % 8 == 0; x 16-byte aligned, q 8-byte
  * aligned, scales 16-byte aligned. M == 0 writes only the scales; K == 0 is a
  * no-op.
- * Memory: when M > 640, a group taller than 640 rows is cut into chunks of
- * at most 640 rows. Each chunk's column maxima go through a device workspace
+ * Memory: a group taller than 896 rows is cut into chunks of at most 896
+ * rows (a tile holds 896 rows of 128 columns: 160 KiB in registers and 64 KiB
+ * in LDS). Each chunk's column maxima go through a device workspace
  * of about (M / 320) * K * 4 bytes, between workgroups of the one kernel
  * launch. A tile that waits for other tiles' maxima waits at most about
  * 20 ms of device wall clock; past that it computes them from x itself, so
@@ -128,7 +129,9 @@ int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
  * Requirements: M % 16 == 0, K % 8 == 0; x and q_t 16-byte aligned,
  * scales_t 4-byte aligned. M == 0 writes only the scales; K == 0 is a
  * no-op. Memory, the bounded wait, graph capture and errors are as for
- * mgs_quant_groups_dim0 (the same tiles).
+ * mgs_quant_groups_dim0, except that tiles hold 640 rows of 128 columns (all
+ * in registers: LDS holds the transposed output stage), so groups taller than
+ * 640 rows are cut into chunks of at most 640 rows.
  */
 int mgs_quant_groups_dim0_t(const void *x, int64_t M, int64_t K,
                             const int32_t *offsets, int32_t n_groups,
@@ -149,7 +152,7 @@ int mgs_quant_groups_dim0_t(const void *x, int64_t M, int64_t K,
  *   scales  (E, D2) fp32, written.
  * Requirements: 1 <= E <= 1024, D1 >= 0, E * D1 < 2^31, D2 % 8 == 0; w
  * 16-byte aligned, q 8-byte aligned, scales 16-byte aligned. Experts taller
- * than 640 rows are cut into chunks exactly as dim0's groups (workspace,
+ * than 896 rows are cut into chunks exactly as dim0's groups (workspace,
  * bounded wait and graph capture as for mgs_quant_groups_dim0).
  */
 int mgs_quant_experts_dim1(const void *w, int64_t E, int64_t D1, int64_t D2,

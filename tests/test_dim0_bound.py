@@ -4,10 +4,12 @@ The dim0 launch has one workgroup per tile and sizes its grid from (M, K, G)
 alone, so the bound must hold for every way of splitting M rows into G
 groups. The tile count of a group depends only on its row count, as a step
 function, so the worst split is found exactly by a knapsack over the first
-row count of each step (0, 81, 161, 321, then 640 * (c - 1) + 1 for the
-groups cut into c >= 2 chunks). The C++ bound, compiled with g++ from the
-header the library uses, must be at least that worst case, for several team
-limits (the most chunks a group may have to be cast as a team)."""
+row count of each step (0, C/8 + 1, C/4 + 1, C/2 + 1, then C * (c - 1) + 1
+for the groups cut into c >= 2 chunks, with C the chunk rows: 896 for the
+dim0 kernel, 640 for the transposed one). The C++ bound, compiled with g++
+from the header the library uses, must be at least that worst case, for
+several team limits (the most chunks a group may have to be cast as a
+team)."""
 import math
 import os
 import subprocess
@@ -23,27 +25,31 @@ DRIVER = r"""
 #include <stdio.h>
 #include "mgs_dim0_layout.hpp"
 int main() {
-    long long M, K, G, T, L;
-    while (scanf("%lld %lld %lld %lld %lld", &M, &K, &G, &T, &L) == 5) {
+    long long M, K, G, T, L, C;
+    while (scanf("%lld %lld %lld %lld %lld %lld", &M, &K, &G, &T, &L, &C) == 6) {
         if (L < 0) {   // the strip-width cap for a device of -L compute units
-            printf("%d\n", mgs::dim0_lt_cap(M, K, G, T, -L));
+            printf("%d\n", mgs::dim0_lt_cap(M, K, G, T, -L, C));
             continue;
         }
-        printf("%lld %lld %lld\n", (long long)mgs::dim0_tile_bound(M, K, G, T, (int)L),
-               (long long)mgs::dim0_chunk_bound(M), (long long)mgs::dim0_group_tiles(M, K, T, (int)L));
+        printf("%lld %lld %lld\n", (long long)mgs::dim0_tile_bound(M, K, G, T, (int)L, C),
+               (long long)mgs::dim0_chunk_bound(M, C),
+               (long long)mgs::dim0_group_tiles(M, K, T, (int)L, C));
     }
     return 0;
 }
 """
 
 
-def tiles(R, K, team_max, max_lt=7):
+CHUNKS = [896, 640]      # chunk rows of the dim0 and dim0_t kernels
+
+
+def tiles(R, K, team_max, max_lt=7, C=896):
     """Tiles of one group of R rows (the rule of the kernel's tile search),
-    with strips at most 8 << max_lt columns wide."""
-    if R > 640:
-        lt, chunks = 4, -(-R // 640)
+    with strips at most 8 << max_lt columns wide and chunks of C rows."""
+    if R > C:
+        lt, chunks = 4, -(-R // C)
     else:
-        lt = 7 if R <= 80 else 6 if R <= 160 else 5 if R <= 320 else 4
+        lt = 7 if R <= C // 8 else 6 if R <= C // 4 else 5 if R <= C // 2 else 4
         chunks = 0
     lt = min(lt, max_lt)
     while lt > 3 and (8 << (lt - 1)) >= K:
@@ -54,10 +60,10 @@ def tiles(R, K, team_max, max_lt=7):
     return (1 if chunks <= team_max else 2) * chunks * ns
 
 
-def worst_splits(Mmax, K, Gmax, team_max, max_lt=7):
+def worst_splits(Mmax, K, Gmax, team_max, max_lt=7, C=896):
     """best[G][M] = the most tiles over all splits of at most M rows into
     exactly G groups."""
-    sizes = [0, 81, 161, 321] + [640 * (c - 1) + 1 for c in range(2, Mmax // 640 + 3)]
+    sizes = [0, C // 8 + 1, C // 4 + 1, C // 2 + 1] + [C * (c - 1) + 1 for c in range(2, Mmax // C + 3)]
     sizes = [r for r in sizes if r <= Mmax]
     NEG = -(1 << 40)
     dp = np.full(Mmax + 1, NEG, np.int64)
@@ -66,7 +72,7 @@ def worst_splits(Mmax, K, Gmax, team_max, max_lt=7):
     for _ in range(Gmax):
         nxt = np.full(Mmax + 1, NEG, np.int64)
         for r in sizes:
-            t = tiles(r, K, team_max, max_lt)
+            t = tiles(r, K, team_max, max_lt, C)
             np.maximum(nxt[r:], dp[:Mmax + 1 - r] + t, out=nxt[r:])
         dp = nxt
         best.append(np.maximum.accumulate(dp))
@@ -83,43 +89,46 @@ def bound_tool():
     subprocess.run(["g++", "-O1", "-std=c++17", "-I", CSRC, "-o", exe, src], check=True)
 
     def run(triples):
-        inp = "".join("%d %d %d %d %d\n" % (t + (7,) if len(t) == 4 else t) for t in triples)
+        inp = "".join("%d %d %d %d %d %d\n" % (tuple(t) + (7, 896)[len(t) - 4:]) for t in triples)
         out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
         return [tuple(int(v) for v in line.split()) for line in out.splitlines()]
     return run
 
 
+@pytest.mark.parametrize("C", CHUNKS)
 @pytest.mark.parametrize("team_max", [1, 3, 26, 128])
 @pytest.mark.parametrize("K", [8, 64, 72, 136, 1032, 8192])
-def test_bound_covers_the_worst_split(bound_tool, K, team_max):
+def test_bound_covers_the_worst_split(bound_tool, K, team_max, C):
     Mmax, Gmax = 17000, 64
-    best = worst_splits(Mmax, K, Gmax, team_max)
-    Ms = [0, 1, 80, 81, 400, 640, 641, 1280, 1281, 1921, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
+    best = worst_splits(Mmax, K, Gmax, team_max, 7, C)
+    Ms = [0, 1, 80, 81, 113, 400, 449, 640, 641, 896, 897, 1280, 1281, 1793, 1921, 5120, 5121, 6000,
+          10242, 12000, 16640, 17000]
     Gs = [1, 2, 3, 7, 16, 64]
-    triples = [(M, K, G, team_max) for M in Ms for G in Gs]
+    triples = [(M, K, G, team_max, 7, C) for M in Ms for G in Gs]
     got = bound_tool(triples)
-    for (M, _, G, _), (b, _, one) in zip(triples, got):
+    for (M, _, G, _, _, _), (b, _, one) in zip(triples, got):
         exact = int(best[G][M])
-        assert b >= exact, (M, K, G, team_max, b, exact)
+        assert b >= exact, (M, K, G, team_max, C, b, exact)
         # and it is no wild over-estimate (the grid's extra workgroups exit at once)
-        assert b <= 2 * exact + 16, (M, K, G, team_max, b, exact)
-        assert one == tiles(M, K, team_max)
+        assert b <= 2 * exact + 16, (M, K, G, team_max, C, b, exact)
+        assert one == tiles(M, K, team_max, 7, C)
 
 
+@pytest.mark.parametrize("C", CHUNKS)
 @pytest.mark.parametrize("max_lt", [3, 4, 5, 6])
 @pytest.mark.parametrize("K", [64, 1032, 4096])
-def test_bound_with_narrowed_strips(bound_tool, K, max_lt):
+def test_bound_with_narrowed_strips(bound_tool, K, max_lt, C):
     team_max = 128
     Mmax, Gmax = 17000, 64
-    best = worst_splits(Mmax, K, Gmax, team_max, max_lt)
-    Ms = [0, 1, 80, 81, 161, 321, 640, 641, 1281, 4096, 6000, 16640, 17000]
+    best = worst_splits(Mmax, K, Gmax, team_max, max_lt, C)
+    Ms = [0, 1, 80, 81, 113, 161, 225, 321, 449, 640, 641, 897, 1281, 4096, 6000, 16640, 17000]
     Gs = [1, 2, 4, 16, 64]
-    triples = [(M, K, G, team_max, max_lt) for M in Ms for G in Gs]
+    triples = [(M, K, G, team_max, max_lt, C) for M in Ms for G in Gs]
     got = bound_tool(triples)
-    for (M, _, G, _, _), (b, _, one) in zip(triples, got):
+    for (M, _, G, _, _, _), (b, _, one) in zip(triples, got):
         exact = int(best[G][M])
-        assert exact <= b <= 2 * exact + 16, (M, K, G, max_lt, b, exact)
-        assert one == tiles(M, K, team_max, max_lt)
+        assert exact <= b <= 2 * exact + 16, (M, K, G, max_lt, C, b, exact)
+        assert one == tiles(M, K, team_max, max_lt, C)
 
 
 def test_strip_cap_policy(bound_tool):
@@ -129,27 +138,31 @@ def test_strip_cap_policy(bound_tool):
     cases = [((4096, 4096, 16), 7), ((256, 4096, 4), 3), ((1024, 2048, 4), 3), ((16640, 8192, 64), 7),
              ((65536, 4096, 8), 7), ((16640, 8192, 1), 7), ((81920, 8192, 16), 7),
              ((4096, 64, 16), 3), ((2048, 8192, 64), 7), ((512, 4096, 8), 4)]
-    got = bound_tool([(M, K, G, 128, -256) for (M, K, G), _ in cases])
-    for ((M, K, G), want), (lt,) in zip(cases, got):
-        assert lt == want, (M, K, G, lt, want)
-        # what the rule promises: a tile per CU for equal groups, unless the
-        # narrowest strips are reached
-        assert lt == 3 or G * tiles(M // G, K, 128, lt) >= 256
+    for C in CHUNKS:
+        got = bound_tool([(M, K, G, 128, -256, C) for (M, K, G), _ in cases])
+        for ((M, K, G), want), (lt,) in zip(cases, got):
+            assert lt == want, (M, K, G, C, lt, want)
+            # what the rule promises: a tile per CU for equal groups, unless the
+            # narrowest strips are reached
+            assert lt == 3 or G * tiles(M // G, K, 128, lt, C) >= 256
 
 
-def test_bound_of_the_benchmark_shape(bound_tool):
-    (b, chunks, _), = bound_tool([(16640, 8192, 64, 128)])
-    exact = int(worst_splits(16640, 8192, 64, 128)[64][16640])
+@pytest.mark.parametrize("C", CHUNKS)
+def test_bound_of_the_benchmark_shape(bound_tool, C):
+    (b, chunks, _), = bound_tool([(16640, 8192, 64, 128, 7, C)])
+    exact = int(worst_splits(16640, 8192, 64, 128, 7, C)[64][16640])
     assert exact <= b
-    assert chunks == 16640 // 640 + 16640 // 641
+    assert chunks == 16640 // C + 16640 // (C + 1)
 
 
-def test_chunk_bound_covers_every_chunked_split(bound_tool):
-    # the chunked groups of any split have at most dim0_chunk_bound(M) chunks
-    for M in (641, 1281, 1282, 1920, 1921, 2562, 5121, 10242, 10243, 16640, 40000):
-        (_, chunks, _), = bound_tool([(M, 8, 1, 128)])
+@pytest.mark.parametrize("C", CHUNKS)
+def test_chunk_bound_covers_every_chunked_split(bound_tool, C):
+    # the chunked groups of any split have at most dim0_chunk_bound(M, C) chunks
+    for M in (C + 1, 2 * C + 1, 2 * C + 2, 3 * C, 3 * C + 1, 4 * C + 2, 8 * C + 1, 16 * C + 2, 16640,
+              40000):
+        (_, chunks, _), = bound_tool([(M, 8, 1, 128, 7, C)])
         worst = 0
-        for n in range(1, M // 641 + 1):            # n groups of just over 640 rows
+        for n in range(1, M // (C + 1) + 1):        # n groups of just over C rows
             rows = M // n
-            worst = max(worst, n * math.ceil(rows / 640))
-        assert chunks >= worst, (M, chunks, worst)
+            worst = max(worst, n * math.ceil(rows / C))
+        assert chunks >= worst, (M, C, chunks, worst)

@@ -1,6 +1,7 @@
 """GPU parity of dim0 where the launch shape matters: the group sizes that
 give the most tiles per row (the grid is an upper bound computed from M, K
-and G alone), groups taller than 640 rows whose column maxima pass between
+and G alone), tiles whose last rows sit in LDS instead of registers, groups
+taller than a chunk (896 rows) whose column maxima pass between
 workgroups of one launch (as a team of chunk tiles, or through
 column-maximum tiles when a group has more chunks than the team limit,
 forced low here through MGS_DIM0_TEAM_MAX), the path that computes those
@@ -59,11 +60,14 @@ def team_env(monkeypatch, team_max):
         monkeypatch.setenv("MGS_DIM0_TEAM_MAX", team_max)
 
 
-# The first row count of each tiling step has the most tiles per row: 81 rows
-# (512-column strips), 161 (256), 321 (128), then 640 * (c - 1) + 1 rows for a
-# group cut into c chunks (641: two). K values leave a ragged last strip.
+# The first row count of each tiling step has the most tiles per row: 113 rows
+# (512-column strips), 225 (256), 449 (128), then 896 * (c - 1) + 1 rows for a
+# group cut into c chunks (897: two); the transposed kernel's steps (81, 161,
+# 321, 641, ...) are covered too. K values leave a ragged last strip.
 @pytest.mark.parametrize("team_max", TEAM_MAX)
 @pytest.mark.parametrize("size,n,K", [
+    (113, 12, 2056), (225, 12, 1032), (449, 8, 520), (897, 6, 264), (1793, 3, 264),
+    (2689, 2, 136), (896, 4, 264), (1792, 3, 136), (112, 10, 1032),
     (81, 12, 2056), (161, 12, 1032), (321, 10, 520), (641, 8, 264), (1281, 4, 264),
     (1921, 3, 136), (5121, 2, 264), (5121, 3, 72), (37, 16, 4104), (577, 4, 264),
     (865, 3, 136), (640, 5, 264), (1280, 3, 136),
@@ -75,10 +79,28 @@ def test_most_tiles_per_row(size, n, K, team_max, monkeypatch):
     check(x, off, "groups of %d rows" % size)
 
 
+# Tiles whose rows run past the 20 register slabs into the LDS slabs, for
+# every strip width: rows 20 * rps .. 28 * rps - 1 (rps = 4, 8, 16, 32 rows
+# per slab), with ragged last slabs, ragged K and empty groups beside them.
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("K,sizes", [
+    (2056, [81, 100, 0, 112, 7]),          # 1024-column strips, rps = 4
+    (1032, [161, 200, 224, 3]),            # 512, rps = 8
+    (520, [321, 400, 448, 16]),            # 256, rps = 16
+    (264, [641, 700, 896, 5, 0]),          # 128, rps = 32
+    (8, [700, 896, 1]),                    # one 8-column strip
+])
+def test_rows_held_in_lds(K, sizes, pow2):
+    off = np.cumsum(sizes).astype(np.int32)
+    x = data(sum(sizes) + K, int(off[-1]), K)
+    check(x, off, "LDS rows %s" % (sizes,), pow2)
+
+
 def test_group_past_the_team_limit():
-    # 141 chunks, more than any team: column-maximum tiles, then casting tiles
-    M, K = 90000, 64
-    check(data(9, M, K), np.array([5, M - 7, M], np.int32), "90000-row group")
+    # 134 chunks of 896 rows, more than any team (at most 128): column-maximum
+    # tiles, then casting tiles
+    M, K = 120000, 64
+    check(data(9, M, K), np.array([5, M - 7, M], np.int32), "120000-row group")
 
 
 def test_many_groups_at_the_group_limit():
@@ -95,6 +117,7 @@ def test_many_groups_at_the_group_limit():
     (11000, 64, [5500, 5500]),
     (3000, 520, [1281, 1719]),
     (2000, 264, [641, 700, 659]),
+    (2700, 264, [897, 1000, 803]),
 ])
 def test_tall_groups_without_the_wait(M, K, sizes, team_max, monkeypatch):
     team_env(monkeypatch, team_max)
