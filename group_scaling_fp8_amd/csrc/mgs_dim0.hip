@@ -155,13 +155,15 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
         t.cbase = 0;
         return;
     }
-    if (t.cls == kClassT) {          // the chunks of a strip together
-        t.strip = local / nc;
-        t.c = local - t.strip * nc;
-    } else {                         // strips fastest
-        t.c = local / ns;
-        t.strip = local - t.c * ns;
-    }
+    // class T: the chunks of a strip together; class C: strips fastest. One
+    // division and plain selects: stores into t.strip or t.c chosen by class
+    // made the compiler keep the Tile in scratch memory.
+    const bool team = t.cls == kClassT;
+    const int den = team ? nc : ns;
+    const int quo = local / den;
+    const int rem = local - quo * den;
+    t.strip = team ? quo : rem;
+    t.c = team ? rem : quo;
     // chunk rows, rounded up to row_align (a power of two; at most 640 still)
     const int cs = ((R + nc - 1) / nc + row_align - 1) & -row_align;
     t.r0 = min(start + t.c * cs, t.g1);
