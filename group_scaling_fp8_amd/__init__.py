@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     MGS_MX_FLOOR, MGS_MX_RCEIL, MGS_OK, MgsError, lib, library_path,
 )
 from .api import (  # noqa: F401
-    mgs_cast_e4m3, mgs_copy, mgs_mx_dequant_dim0, mgs_mx_quant_dim0, mgs_mx_quant_dim1, mgs_quant_groups_dim0, mgs_quant_groups_dim0_t,
-    mgs_quant_experts_dim1, mgs_quant_groups_dim1,
+    dim0_workspace, mgs_cast_e4m3, mgs_copy, mgs_dim0_workspace_bytes, mgs_mx_dequant_dim0,
+    mgs_mx_quant_dim0, mgs_mx_quant_dim1, mgs_quant_experts_dim1, mgs_quant_groups_dim0,
+    mgs_quant_groups_dim0_t, mgs_quant_groups_dim1,
 )

@@ -20,10 +20,11 @@ MGS_MAX_GROUPS = 1024
 MGS_DIM1_MAX_K = 131072
 
 EXPORTS = (
-    "mgs_quant_groups_dim0", "mgs_quant_groups_dim0_t", "mgs_quant_experts_dim1",
+    "mgs_quant_groups_dim0", "mgs_dim0_workspace_bytes", "mgs_quant_groups_dim0_ws",
+    "mgs_quant_groups_dim0_t", "mgs_quant_experts_dim1",
     "mgs_quant_groups_dim1", "mgs_mx_quant_dim0",
     "mgs_mx_quant_dim1", "mgs_mx_dequant_dim0", "mgs_cast_e4m3",
-    "mgs_copy", "mgs_status_string", "mgs_last_hip_error",
+    "mgs_copy", "mgs_test_quant_dim0", "mgs_status_string", "mgs_last_hip_error",
 )
 
 _lock = threading.Lock()
@@ -54,14 +55,23 @@ def lib():
                 "g.build()'` or `python group_scaling_fp8_amd/build.py`" % _LIB_PATH)
         L = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
-        for name in ("mgs_quant_groups_dim0", "mgs_quant_groups_dim0_t", "mgs_quant_groups_dim1"):
+        for name in ("mgs_quant_groups_dim0", "mgs_quant_groups_dim1"):
             fn = getattr(L, name)
             fn.argtypes = [vp, i64, i64, vp, i32, u32, vp, vp, vp]
             fn.restype = ctypes.c_int
+        for name in ("mgs_quant_groups_dim0_ws", "mgs_quant_groups_dim0_t"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp, i64, i64, vp, i32, u32, vp, vp, vp, i64, vp]
+            fn.restype = ctypes.c_int
+        L.mgs_dim0_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(i64)]
+        L.mgs_dim0_workspace_bytes.restype = ctypes.c_int
         L.mgs_mx_quant_dim0.argtypes = [vp, i64, i64, vp, i32, ctypes.c_int, vp, vp, vp]
         L.mgs_mx_quant_dim0.restype = ctypes.c_int
-        L.mgs_quant_experts_dim1.argtypes = [vp, i64, i64, i64, u32, vp, vp, vp]
+        L.mgs_quant_experts_dim1.argtypes = [vp, i64, i64, i64, u32, vp, vp, vp, i64, vp]
         L.mgs_quant_experts_dim1.restype = ctypes.c_int
+        L.mgs_test_quant_dim0.argtypes = [vp, i64, i64, vp, i32, i64, u32, ctypes.c_int, vp, vp, vp,
+                                          i64, i64, i32, vp]
+        L.mgs_test_quant_dim0.restype = ctypes.c_int
         L.mgs_mx_quant_dim1.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp]
         L.mgs_mx_quant_dim1.restype = ctypes.c_int
         L.mgs_mx_dequant_dim0.argtypes = [vp, vp, i64, i64, vp, vp]

@@ -50,28 +50,64 @@ def _flags(pow2: bool, validate: bool) -> int:
     return (MGS_FLAG_POW2_SCALE if pow2 else 0) | (MGS_FLAG_VALIDATE if validate else 0)
 
 
+def mgs_dim0_workspace_bytes(M: int, K: int) -> int:
+    """Bytes of workspace the dim0-family calls need for an (M, K) input
+    (0 when no group can be cut into chunks)."""
+    import ctypes
+    n = ctypes.c_int64(0)
+    check("mgs_dim0_workspace_bytes", lib().mgs_dim0_workspace_bytes(int(M), int(K), ctypes.byref(n)))
+    return int(n.value)
+
+
+def dim0_workspace(M: int, K: int, device=None) -> torch.Tensor:
+    """A zero-filled workspace for dim0-family calls on (M, K) inputs (any
+    smaller shape fits too). Keep it for reuse: calls leave it valid."""
+    n = mgs_dim0_workspace_bytes(M, K)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def _ws_args(workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return None, 0
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
                           q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
-                          stream=None, validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+                          stream=None, validate: bool = False,
+                          workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-group scaling along dim0: x (M, K) bf16, int32 end offsets over M.
-    Returns q (M, K) uint8 E4M3 and scales (G, K) float32."""
+    Returns q (M, K) uint8 E4M3 and scales (G, K) float32. With `workspace`
+    (from dim0_workspace) it calls mgs_quant_groups_dim0_ws, else
+    mgs_quant_groups_dim0 (the library's own workspace)."""
     _need(x, "x", _BF16_LIKE, 2)
     _need(offsets, "offsets", (torch.int32,), 1)
     M, K = x.shape
     G = offsets.shape[0]
     q = _out(q, (M, K), torch.uint8, x.device, "q")
     scales = _out(scales, (G, K), torch.float32, x.device, "scales")
-    st = lib().mgs_quant_groups_dim0(x.data_ptr(), M, K, offsets.data_ptr(), G,
-                                     _flags(pow2, validate), q.data_ptr(),
-                                     scales.data_ptr(), _stream_handle(stream))
-    check("mgs_quant_groups_dim0", st)
+    if workspace is None:
+        st = lib().mgs_quant_groups_dim0(x.data_ptr(), M, K, offsets.data_ptr(), G,
+                                         _flags(pow2, validate), q.data_ptr(),
+                                         scales.data_ptr(), _stream_handle(stream))
+        check("mgs_quant_groups_dim0", st)
+    else:
+        wp, wb = _ws_args(workspace)
+        st = lib().mgs_quant_groups_dim0_ws(x.data_ptr(), M, K, offsets.data_ptr(), G,
+                                            _flags(pow2, validate), q.data_ptr(),
+                                            scales.data_ptr(), wp, wb, _stream_handle(stream))
+        check("mgs_quant_groups_dim0_ws", st)
     return q, scales
 
 
 def mgs_quant_groups_dim0_t(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
                             q_t: Optional[torch.Tensor] = None,
                             scales_t: Optional[torch.Tensor] = None, stream=None,
-                            validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+                            validate: bool = False,
+                            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-group scaling along dim0 with transposed outputs: x (M, K) bf16,
     int32 end offsets over M (multiples of 16). Returns q_t (K, M) uint8
     E4M3 and scales_t (K, G) float32, the transposes of dim0's outputs."""
@@ -81,24 +117,26 @@ def mgs_quant_groups_dim0_t(x: torch.Tensor, offsets: torch.Tensor, pow2: bool =
     G = offsets.shape[0]
     q_t = _out(q_t, (K, M), torch.uint8, x.device, "q_t")
     scales_t = _out(scales_t, (K, G), torch.float32, x.device, "scales_t")
+    wp, wb = _ws_args(workspace)
     st = lib().mgs_quant_groups_dim0_t(x.data_ptr(), M, K, offsets.data_ptr(), G,
                                        _flags(pow2, validate), q_t.data_ptr(),
-                                       scales_t.data_ptr(), _stream_handle(stream))
+                                       scales_t.data_ptr(), wp, wb, _stream_handle(stream))
     check("mgs_quant_groups_dim0_t", st)
     return q_t, scales_t
 
 
 def mgs_quant_experts_dim1(w: torch.Tensor, pow2: bool = False, q: Optional[torch.Tensor] = None,
-                           scales: Optional[torch.Tensor] = None,
-                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                           scales: Optional[torch.Tensor] = None, stream=None,
+                           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-expert scaling of a 3D weight w (E, D1, D2) bf16 along dim 1.
     Returns q (E, D1, D2) uint8 E4M3 and scales (E, D2) float32."""
     _need(w, "w", _BF16_LIKE, 3)
     E, D1, D2 = w.shape
     q = _out(q, (E, D1, D2), torch.uint8, w.device, "q")
     scales = _out(scales, (E, D2), torch.float32, w.device, "scales")
+    wp, wb = _ws_args(workspace)
     st = lib().mgs_quant_experts_dim1(w.data_ptr(), E, D1, D2, MGS_FLAG_POW2_SCALE if pow2 else 0,
-                                      q.data_ptr(), scales.data_ptr(), _stream_handle(stream))
+                                      q.data_ptr(), scales.data_ptr(), wp, wb, _stream_handle(stream))
     check("mgs_quant_experts_dim1", st)
     return q, scales
 
@@ -202,3 +240,31 @@ def mgs_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
     st = lib().mgs_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream))
     check("mgs_copy", st)
     return dst
+
+
+# Default wait bound and team limit for _test_quant_dim0 (below -1 and 0).
+TEST_DEFAULT_SPIN = -2
+TEST_DEFAULT_TEAM = 0
+
+
+def _test_quant_dim0(x: torch.Tensor, offsets: Optional[torch.Tensor], q: torch.Tensor,
+                     scales: torch.Tensor, pow2: bool = False, transposed: bool = False,
+                     uniform_rows: int = -1, n_groups: Optional[int] = None,
+                     spin_ticks: int = TEST_DEFAULT_SPIN, team_max: int = TEST_DEFAULT_TEAM,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Test-only: mgs_test_quant_dim0 (the dim0-family call with the wait
+    bound and the team limit overridden). x is 2D (M, K); for equal groups
+    pass offsets=None, uniform_rows and n_groups."""
+    _need(x, "x", _BF16_LIKE, 2)
+    M, K = x.shape
+    if offsets is not None:
+        _need(offsets, "offsets", (torch.int32,), 1)
+        off_ptr, G = offsets.data_ptr(), offsets.shape[0]
+    else:
+        off_ptr, G = None, int(n_groups)
+    wp, wb = _ws_args(workspace)
+    st = lib().mgs_test_quant_dim0(x.data_ptr(), M, K, off_ptr, G, int(uniform_rows),
+                                   MGS_FLAG_POW2_SCALE if pow2 else 0, 1 if transposed else 0,
+                                   q.data_ptr(), scales.data_ptr(), wp, wb, int(spin_ticks),
+                                   int(team_max), _stream_handle(stream))
+    check("mgs_test_quant_dim0", st)

@@ -2,8 +2,8 @@
 // argument checks, the dim0 workspace, and stream-ordered launches.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -24,66 +24,47 @@ int hip_status(hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Device workspace of dim0 for groups taller than 640 rows (layout in
-// Dim0Workspace), one per (device, stream) so that concurrent streams never
-// share it. It grows on demand and lives until process exit. gen is the last
-// generation number handed to a kernel on that stream (1 .. 2^31 - 1).
+// The library's own dim0 workspace, used only by calls that pass none: one
+// per (device, stream), so that calls on different streams never share one.
+// It only grows. A grown workspace replaces the old one for later calls, but
+// the old buffer is kept until process exit (graphs captured earlier may
+// still use it), so nothing is ever freed and nothing waits for the stream.
+// A new buffer is zero-filled by a kernel queued on the stream before the
+// call's own kernel.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
-    uint32_t gen = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace>* g_ws = nullptr;
+std::vector<void*>* g_ws_retired = nullptr;
 
-// Returns the workspace of the current device and `stream` with at least
-// `bytes` bytes and the generation number of this call (0 when the stream is
-// capturing a graph: then the kernel reads it from the epoch word).
-// A new or regrown buffer is zeroed in stream order, and so is the whole
-// buffer whenever the host counter wraps.
-hipError_t dim0_workspace_for(hipStream_t stream, const mgs::Dim0Workspace& layout, bool capturing,
-                              void** out, uint32_t* gen) {
+hipError_t own_workspace(hipStream_t stream, size_t need, bool capturing, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
+    if (!g_ws) {
+        g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
+        g_ws_retired = new std::vector<void*>();
+    }
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
-    if (w.bytes < layout.bytes) {
+    if (w.bytes < need) {
         // no allocation while a graph is being captured
         if (capturing) return hipErrorStreamCaptureUnsupported;
-        if (w.ptr) {
-            // earlier work on this stream may still read the old buffer
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return e;
-            e = hipFree(w.ptr);
-            if (e != hipSuccess) return e;
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        e = hipMalloc(&w.ptr, layout.bytes);
+        void* p = nullptr;
+        e = hipMalloc(&p, need);
+        if (e != hipSuccess) return e;
+        e = mgs::launch_zero(p, need, stream);
         if (e != hipSuccess) {
-            w.ptr = nullptr;
+            g_ws_retired->push_back(p);
             return e;
         }
-        e = hipMemsetAsync(w.ptr, 0, layout.bytes, stream);
-        if (e != hipSuccess) return e;
-        w.bytes = layout.bytes;
-        w.gen = 0;
+        if (w.ptr) g_ws_retired->push_back(w.ptr);
+        w.ptr = p;
+        w.bytes = need;
     }
     *out = w.ptr;
-    if (capturing) {
-        *gen = 0;
-        return hipSuccess;
-    }
-    if (w.gen >= 0x7FFFFFFFu) {
-        // wrapped: clear the workspace so that no stale word can hold the
-        // next generation
-        e = hipMemsetAsync(w.ptr, 0, w.bytes, stream);
-        if (e != hipSuccess) return e;
-        w.gen = 0;
-    }
-    *gen = ++w.gen;
     return hipSuccess;
 }
 
@@ -139,113 +120,148 @@ struct DeviceInfo {
     int cus;                // compute units
 };
 
+// Per-device constants, read from the runtime once per device. Two threads
+// may both fill an entry the first time; they write the same values.
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev_info[kMaxDevices];
+std::atomic<int> g_dev_ready[kMaxDevices];
+
 DeviceInfo device_info() {
-    static std::mutex mu;
-    static std::map<int, DeviceInfo> per_device;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DeviceInfo{2000000, 1, 1};
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = per_device.find(dev);
-    if (it != per_device.end()) return it->second;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return DeviceInfo{2000000, 1, 1};
+    if (g_dev_ready[dev].load(std::memory_order_acquire)) return g_dev_info[dev];
     int khz = 0, cus = 0;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
         khz = 100000;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 1;
-    DeviceInfo d{20LL * khz, cus < kDim0MaxTeam ? cus : kDim0MaxTeam, cus};
-    per_device[dev] = d;
+    const DeviceInfo d{20LL * khz, cus < kDim0MaxTeam ? cus : kDim0MaxTeam, cus};
+    g_dev_info[dev] = d;
+    g_dev_ready[dev].store(1, std::memory_order_release);
     return d;
 }
 
-// Bound on a dim0 tile's wait for maxima written by other tiles: 20 ms of
-// device wall clock. MGS_DIM0_SPIN_TICKS overrides it (a negative value
-// skips the wait, which exercises the path where a tile computes the maxima
-// itself).
-long long dim0_spin_ticks(const DeviceInfo& d) {
-    if (const char* v = getenv("MGS_DIM0_SPIN_TICKS")) return atoll(v);
-    return d.spin_ticks;
-}
+// Overrides of two dim0 launch parameters, for tests only (mgs_test_quant_dim0).
+struct Dim0Knobs {
+    long long spin_ticks;   // wait bound in wall-clock ticks; -1: no wait; below -1: the default
+    int team_max;           // 1 .. the device's limit lowers it (taller groups go to class C); else the default
+};
 
-// Most chunks of a group cast as a team: min(128, CU count).
-// MGS_DIM0_TEAM_MAX lowers it (at least 1), which sends tall groups through
-// the column-maximum tiles instead.
-int dim0_team_max(const DeviceInfo& d) {
-    if (const char* v = getenv("MGS_DIM0_TEAM_MAX")) {
-        const int t = atoi(v);
-        if (t >= 1 && t < d.team_max) return t;
-    }
-    return d.team_max;
-}
-
-// Both dim0 entry points: q (M, K) and scales (G, K), or their transposes.
-// uniform_rows >= 0: n_groups equal groups of uniform_rows rows and no offsets.
+// Every dim0-family entry point: q (M, K) and scales (G, K), or their
+// transposes. uniform_rows >= 0: n_groups equal groups of uniform_rows rows
+// and no offsets. ws == null && ws_bytes == 0: the library's own workspace.
 int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
-                      int32_t n_groups, uint32_t flags, void* q, float* scales, void* stream,
-                      bool transposed, int64_t uniform_rows = -1) {
+                      int32_t n_groups, uint32_t flags, void* q, float* scales, void* ws,
+                      int64_t ws_bytes, void* stream, bool transposed, int64_t uniform_rows,
+                      const Dim0Knobs* knobs) {
     const bool uniform = uniform_rows >= 0;
     int st = check_grouped(x, M, K, uniform ? kNoOffsets : offsets, n_groups, flags, q, scales);
     if (st != MGS_OK) return st;
     if (K % 8 != 0) return MGS_ERR_INVALID_ARG;
     if (transposed && (M % 16 != 0 || (M * K > 0 && !aligned(q, 16)))) return MGS_ERR_INVALID_ARG;
+    if (ws_bytes < 0 || (!ws && ws_bytes != 0) || (ws && !aligned(ws, 256))) return MGS_ERR_INVALID_ARG;
     if (K == 0) return MGS_OK;
     if (!scales || !aligned(scales, transposed ? 4 : 16)) return MGS_ERR_INVALID_ARG;
+    const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);
+    if (ws && (size_t)ws_bytes < layout.bytes) return MGS_ERR_INVALID_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((flags & MGS_FLAG_VALIDATE) && !uniform) {
-        st = validate_offsets(offsets, n_groups, M, transposed ? 16 : 1,
-                              reinterpret_cast<hipStream_t>(stream));
+        st = validate_offsets(offsets, n_groups, M, transposed ? 16 : 1, s);
         if (st != MGS_OK) return st;
     }
     const mgs::DeviceInfo dinfo = mgs::device_info();
-    const int team_max = mgs::dim0_team_max(dinfo);
+    int team_max = dinfo.team_max;
+    long long spin_ticks = dinfo.spin_ticks;
+    if (knobs) {
+        if (knobs->team_max >= 1 && knobs->team_max < team_max) team_max = knobs->team_max;
+        if (knobs->spin_ticks >= -1) spin_ticks = knobs->spin_ticks;
+    }
     const int64_t chunk_rows = transposed ? mgs::kDim0ChunkRowsT : mgs::kDim0ChunkRows;
     const int lt_cap = mgs::dim0_lt_cap(M, K, n_groups, team_max, dinfo.cus, chunk_rows);
     if (mgs::dim0_tile_bound(M, K, n_groups, team_max, lt_cap, chunk_rows) >= INT32_MAX)
         return MGS_ERR_UNSUPPORTED;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);
-    void* ws = nullptr;
-    uint32_t gen = 0;
-    if (layout.chunks > 0) {
+    void* w = ws;
+    if (layout.bytes == 0) {
+        w = nullptr;            // no chunked group possible: the kernels never touch it
+    } else if (!w) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         hipError_t e = hipStreamIsCapturing(s, &cap);
         if (e != hipSuccess) return hip_status(e);
-        const bool capturing = cap != hipStreamCaptureStatusNone;
-        e = dim0_workspace_for(s, layout, capturing, &ws, &gen);
+        e = own_workspace(s, layout.bytes, cap != hipStreamCaptureStatusNone, &w);
         if (e == hipErrorStreamCaptureUnsupported) return MGS_ERR_UNSUPPORTED;
         if (e != hipSuccess) return hip_status(e);
-        if (capturing) {
-            e = mgs::launch_dim0_epoch_bump(ws, s);
-            if (e != hipSuccess) return hip_status(e);
-        }
     }
     return hip_status(mgs::launch_dim0(static_cast<const uint16_t*>(x), (int)M, (int)K, offsets,
                                        n_groups, (int)uniform_rows,
                                        (flags & MGS_FLAG_POW2_SCALE) != 0, transposed,
-                                       static_cast<uint8_t*>(q), scales, team_max, lt_cap, ws, gen,
-                                       mgs::dim0_spin_ticks(dinfo), s));
+                                       static_cast<uint8_t*>(q), scales, team_max, lt_cap, w, spin_ticks,
+                                       s));
+}
+
+int quant_experts(const void* w, int64_t E, int64_t D1, int64_t D2, uint32_t flags, void* q,
+                  float* scales, void* ws, int64_t ws_bytes, void* stream, const Dim0Knobs* knobs) {
+    if (E < 1 || D1 < 0) return MGS_ERR_INVALID_ARG;
+    if (E > MGS_MAX_GROUPS || D1 > INT32_MAX / E) return MGS_ERR_UNSUPPORTED;
+    return quant_groups_dim0(w, E * D1, D2, nullptr, (int32_t)E, flags, q, scales, ws, ws_bytes, stream,
+                             false, D1, knobs);
 }
 
 }  // namespace mgs
 
 extern "C" {
 
+int mgs_dim0_workspace_bytes(int64_t M, int64_t K, int64_t* bytes) {
+    if (!bytes || M < 0 || K < 0) return MGS_ERR_INVALID_ARG;
+    if (M > INT32_MAX || K > INT32_MAX) return MGS_ERR_UNSUPPORTED;
+    *bytes = (int64_t)mgs::dim0_workspace(M, K).bytes;
+    return MGS_OK;
+}
+
 int mgs_quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
                           int32_t n_groups, uint32_t flags, void* q, float* scales,
                           void* stream) {
-    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q, scales, stream, false);
+    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q, scales, nullptr, 0, stream,
+                                  false, -1, nullptr);
+}
+
+int mgs_quant_groups_dim0_ws(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                             int32_t n_groups, uint32_t flags, void* q, float* scales,
+                             void* workspace, int64_t workspace_bytes, void* stream) {
+    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q, scales, workspace,
+                                  workspace_bytes, stream, false, -1, nullptr);
 }
 
 int mgs_quant_groups_dim0_t(const void* x, int64_t M, int64_t K, const int32_t* offsets,
                             int32_t n_groups, uint32_t flags, void* q_t, float* scales_t,
-                            void* stream) {
-    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q_t, scales_t, stream, true);
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q_t, scales_t, workspace,
+                                  workspace_bytes, stream, true, -1, nullptr);
 }
 
 int mgs_quant_experts_dim1(const void* w, int64_t E, int64_t D1, int64_t D2, uint32_t flags,
-                           void* q, float* scales, void* stream) {
-    if (E < 1 || D1 < 0) return MGS_ERR_INVALID_ARG;
-    if (E > MGS_MAX_GROUPS || D1 > INT32_MAX / E) return MGS_ERR_UNSUPPORTED;
-    return mgs::quant_groups_dim0(w, E * D1, D2, nullptr, (int32_t)E, flags, q, scales, stream, false,
-                                  D1);
+                           void* q, float* scales, void* workspace, int64_t workspace_bytes,
+                           void* stream) {
+    return mgs::quant_experts(w, E, D1, D2, flags, q, scales, workspace, workspace_bytes, stream,
+                              nullptr);
+}
+
+int mgs_test_quant_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                        int32_t n_groups, int64_t uniform_rows, uint32_t flags, int transposed,
+                        void* q, float* scales, void* workspace, int64_t workspace_bytes,
+                        int64_t spin_ticks, int32_t team_max, void* stream) {
+    const mgs::Dim0Knobs knobs{(long long)spin_ticks, (int)team_max};
+    if (uniform_rows >= 0) {
+        if (transposed) return MGS_ERR_INVALID_ARG;
+        if (M < 0 || (uniform_rows > 0 && M % uniform_rows != 0) || (uniform_rows == 0 && M != 0))
+            return MGS_ERR_INVALID_ARG;
+        const int64_t E = n_groups;
+        if (uniform_rows * E != M) return MGS_ERR_INVALID_ARG;
+        return mgs::quant_experts(x, E, uniform_rows, K, flags, q, scales, workspace, workspace_bytes,
+                                  stream, &knobs);
+    }
+    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q, scales, workspace,
+                                  workspace_bytes, stream, transposed != 0, -1, &knobs);
 }
 
 int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* offsets,
@@ -287,7 +303,7 @@ int mgs_mx_quant_dim1(const void* x, int64_t M, int64_t K, int mode, void* q_t, 
     if (mode != MGS_MX_FLOOR && mode != MGS_MX_RCEIL) return MGS_ERR_INVALID_ARG;
     if (M == 0 || K == 0) return MGS_OK;
     if (M > INT64_MAX / K) return MGS_ERR_UNSUPPORTED;
-    if (!x || !q_t || !scales_t || !aligned(x, 16) || !aligned(q_t, 8)) return MGS_ERR_INVALID_ARG;
+    if (!x || !q_t || !scales_t || !aligned(x, 16) || !aligned(q_t, 16)) return MGS_ERR_INVALID_ARG;
     return hip_status(mgs::launch_mx_dim1(static_cast<const uint16_t*>(x), M, K, mode == MGS_MX_RCEIL,
                                           static_cast<uint8_t*>(q_t), scales_t,
                                           reinterpret_cast<hipStream_t>(stream)));

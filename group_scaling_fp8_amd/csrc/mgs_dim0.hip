@@ -44,13 +44,19 @@
 //     tile per (chunk, strip). All column-maximum tiles come first in the
 //     grid; a casting tile waits for its strip's maxima before its own loads,
 //     and casts its chunk (a chunk is read twice).
-// Maxima go through the workspace as 64-bit words, each holding the call's
-// generation number next to the maxima of two columns, written and read as
-// single relaxed device-scope atomics. A word is read and written whole, so
-// a reader that sees the current generation sees that call's maxima: no
-// fence or flag is needed. Every wait is bounded: past it the tile computes
-// the column amax of the whole group from x itself, so the result never
-// depends on the order in which workgroups run.
+// Maxima go through the workspace as 64-bit words, each holding a presence
+// tag next to the maxima of two columns, written and read as single relaxed
+// device-scope atomics. A word is read and written whole, so a reader that
+// sees the tag sees the maxima: no fence or flag is needed. Every wait is
+// bounded: past it the tile computes the column amax of the whole group from
+// x itself, so the result never depends on the order in which workgroups run.
+// The workspace is all zero between launches, so a tagged word can only be
+// this launch's. Every tile of a team (a chunked group on one strip: its
+// chunk tiles, and in class C its column-maximum tiles) counts itself on the
+// team's counter once it has read every word it needs and its own words are
+// stored; the counter wraps back to zero on the team's last tile, which then
+// clears the team's words. No state outlives a launch, so calls need nothing
+// from the host, and a captured graph replays with no extra node.
 // Tile order: all column-maximum tiles, then every group's own tiles in
 // group order: class A strip by strip; class T strip by strip with the chunks
 // of a strip together; class C chunk by chunk with strips fastest.
@@ -388,6 +394,23 @@ __device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Tag of a word that holds this launch's maxima (the workspace is zero
+// between launches).
+constexpr uint64_t kWordPresent = uint64_t(1) << 32;
+
+// Wave 0 of a tile of a team, after the tile's last read of maxima words and
+// once its own words are stored: counts the tile on the team's counter, which
+// wraps to zero on the team's last tile (an atomic increment with bound
+// team_size - 1). Returns the count before (lane 0); the value is first used
+// after the tile's final barrier, so the increment's round trip overlaps the
+// tile's stores.
+__device__ __forceinline__ uint32_t team_tile_done(uint32_t* ctr, uint32_t team_size) {
+    uint32_t old = 0;
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        old = __builtin_amdgcn_atomic_inc32(ctr, team_size - 1u, __ATOMIC_RELAXED, "agent");
+    return old;
+}
+
 // The words of this lane's 8 columns for chunk c of the tile's group.
 __device__ __forceinline__ uint64_t* chunk_words(uint64_t* ws_max, const Tile& t, int c, int64_t K,
                                                  const TileGeom& q) {
@@ -396,23 +419,32 @@ __device__ __forceinline__ uint64_t* chunk_words(uint64_t* ws_max, const Tile& t
 
 // Publishes this chunk's column maxima (threads 0..tpr-1 hold them).
 __device__ __forceinline__ void publish_maxima(uint64_t* ws_max, const Tile& t, int64_t K,
-                                               const TileGeom& q, uint4 m, uint32_t gen) {
+                                               const TileGeom& q, uint4 m) {
     if (threadIdx.x < q.tpr && q.col_ok) {
         uint64_t* dst = chunk_words(ws_max, t, t.c, K, q);
-        const uint64_t g = (uint64_t)gen << 32;
-        store_agent(dst, g | m.x);
-        store_agent(dst + 1, g | m.y);
-        store_agent(dst + 2, g | m.z);
-        store_agent(dst + 3, g | m.w);
+        store_agent(dst, kWordPresent | m.x);
+        store_agent(dst + 1, kWordPresent | m.y);
+        store_agent(dst + 2, kWordPresent | m.z);
+        store_agent(dst + 3, kWordPresent | m.w);
     }
 }
 
+// Wave 0 of the team's last tile: clears the words of the team's chunk rows
+// in its strip (one word per column pair: 4 << lt words per row, at most 64
+// since chunked groups have strips of at most 128 columns).
+__device__ __forceinline__ void clear_team_words(uint64_t* ws_max, const Tile& t, int64_t K) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int per_strip = 4 << t.lt;
+    const int64_t w = (int64_t)t.strip * per_strip + lane;
+    if (lane >= per_strip || w >= K / 2) return;
+    for (int c = 0; c < t.nc; ++c) store_agent(ws_max + (int64_t)(t.cbase + c) * (K / 2) + w, 0ull);
+}
+
 // Folds into m the maxima of chunks ty, ty + rps, ... of the tile's strip,
-// waiting until each word carries `gen`. Returns false if the wait ran out
+// waiting until each word is present. Returns false if the wait ran out
 // (then m is incomplete) or was skipped (spin_ticks < 0).
 __device__ __forceinline__ bool gather_maxima(uint64_t* ws_max, const Tile& t, int64_t K,
-                                              const TileGeom& q, uint32_t gen, long long spin_ticks,
-                                              uint4& m) {
+                                              const TileGeom& q, long long spin_ticks, uint4& m) {
     if (spin_ticks < 0) return false;
     if (!q.col_ok) return true;
     const long long t0 = wall_clock64();
@@ -424,9 +456,7 @@ __device__ __forceinline__ bool gather_maxima(uint64_t* ws_max, const Tile& t, i
             w1 = load_agent(src + 1);
             w2 = load_agent(src + 2);
             w3 = load_agent(src + 3);
-            if ((uint32_t)(w0 >> 32) == gen && (uint32_t)(w1 >> 32) == gen &&
-                (uint32_t)(w2 >> 32) == gen && (uint32_t)(w3 >> 32) == gen)
-                break;
+            if ((w0 & w1 & w2 & w3) & kWordPresent) break;
             if (wall_clock64() - t0 > spin_ticks) return false;
             __builtin_amdgcn_s_sleep(8);
         }
@@ -454,26 +484,34 @@ template <bool kT>
 __device__ __forceinline__ void dim0_body(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
-        int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks, int uniform_rows, uint4* red, uint32_t* stage,
-        uint4* ext) {
+        int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
+        long long spin_ticks, int uniform_rows, uint4* red, uint32_t* stage, uint4* ext) {
     constexpr int kRowAlign = kT ? 16 : 1;
+    constexpr int kRows = rows_w128<kT>();
+    const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x) < kWave;
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile<rows_w128<kT>()>(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign,
-                                                   uniform_rows, (int)item);
+        const Tile t = find_tile<kRows>(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign,
+                                        uniform_rows, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);
         const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
-        const uint32_t gen = t.cls == kClassA ? 0u : (gen_arg ? gen_arg : *ws_epoch);
+        // a team: the tiles of one chunked group on one strip (class C: its
+        // column-maximum tiles too), with one counter in the workspace
+        const bool chunked = t.cls != kClassA;
+        const uint32_t team_size = t.cls == kClassT ? (uint32_t)t.nc : 2u * (uint32_t)t.nc;
+        // (strips of chunked groups are 128 columns wide, or 64 in launches
+        // that narrow every strip; a chunked group has at least two chunk
+        // rows, so its ceil(K / 64) counters fit in its rows' slots)
+        uint32_t* team_ctr = ws_ctr + (int64_t)t.cbase * ((K + 127) >> 7) + t.strip;
 
         uint4 m = make_uint4(0u, 0u, 0u, 0u);
         if (t.cls == kClassC && !t.maxima) {
             // casting tile of a class C group: its strip's maxima were written
             // by tiles earlier in the grid; wait for them before the tile's own
             // loads, so that no tile data sits in registers meanwhile
-            const bool ok = gather_maxima(ws_max, t, K, geo, gen, spin_ticks, m);
+            const bool ok = gather_maxima(ws_max, t, K, geo, spin_ticks, m);
             if (!__syncthreads_and(ok)) {
                 m = make_uint4(0u, 0u, 0u, 0u);
                 stream_amax(x, K, t.g0, t.g1 - t.g0, geo, m);
@@ -502,21 +540,32 @@ __device__ __forceinline__ void dim0_body(
         if (t.maxima) {
             // class C column-maximum tile: publish this chunk's column maxima
             m = block_column_amax(m, geo.tpr, red);
-            publish_maxima(ws_max, t, K, geo, m, gen);
-            __syncthreads();
-            continue;     // the barrier above ends this item's reads of red
+            publish_maxima(ws_max, t, K, geo, m);
+            uint32_t before = 0;
+            if (wave0) {
+                // this wave's words are stored before the tile counts as done
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                before = team_tile_done(team_ctr, team_size);
+            }
+            __syncthreads();      // ends this item's reads of red
+            if (wave0 && __builtin_amdgcn_readfirstlane(before) + 1u == team_size)
+                clear_team_words(ws_max, t, K);
+            continue;
         }
         if (t.cls == kClassT) {
             // team tile: publish this chunk's maxima, then combine the team's
             m = block_column_amax(m, geo.tpr, red);
-            publish_maxima(ws_max, t, K, geo, m, gen);
+            publish_maxima(ws_max, t, K, geo, m);
             m = make_uint4(0u, 0u, 0u, 0u);
-            const bool ok = gather_maxima(ws_max, t, K, geo, gen, spin_ticks, m);
+            // a complete gather has read this tile's own words back, so they
+            // are stored before the tile counts as done
+            const bool ok = gather_maxima(ws_max, t, K, geo, spin_ticks, m);
             if (!__syncthreads_and(ok)) {
                 // the team's maxima did not come in time: the column amax of
                 // the whole group from x
                 m = make_uint4(0u, 0u, 0u, 0u);
                 stream_amax(x, K, t.g0, t.g1 - t.g0, geo, m);
+                if (wave0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
         }
         m = block_column_amax(m, geo.tpr, red);
@@ -619,71 +668,76 @@ __device__ __forceinline__ void dim0_body(
                 }
             }
         }
+        uint32_t before = 0;
+        if (chunked && wave0) before = team_tile_done(team_ctr, team_size);
         __syncthreads();     // red (and the stage) are rewritten by the next item
+        if (chunked && wave0 && __builtin_amdgcn_readfirstlane(before) + 1u == team_size)
+            clear_team_words(ws_max, t, K);
     }
 }
 
 }  // namespace
 
-// ws layout (Dim0Workspace): the epoch word, then maxima[chunk][K / 2]
-// 64-bit words (generation << 32 | two 16-bit magnitude patterns).
+// ws layout (Dim0Workspace): a counter per (chunk row, 128-column strip),
+// then maxima[chunk row][K / 2] 64-bit words (presence tag << 32 | two 16-bit
+// magnitude patterns).
 __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
-        int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks, int uniform_rows) {
+        int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
+        long long spin_ticks, int uniform_rows) {
     __shared__ uint4 red[kThreads];
     __shared__ uint4 ext[kLdsSlabs * kThreads];     // 64 KiB: the tile's rows past the registers
-    dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
-                     ws_max, gen_arg, spin_ticks, uniform_rows, red, nullptr, ext);
+    dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
+                     ws_max, spin_ticks, uniform_rows, red, nullptr, ext);
 }
 
 // The same per-group scaling with transposed outputs: qT (K, M), scalesT (K, G).
 __global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
-        int lt_cap, int maybe_c, const uint32_t* __restrict__ ws_epoch, uint64_t* __restrict__ ws_max,
-        uint32_t gen_arg, long long spin_ticks, int uniform_rows) {
+        int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
+        long long spin_ticks, int uniform_rows) {
     __shared__ uint4 red[kThreads];
     __shared__ uint4 stage[kStageWords / 4];
-    dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_epoch,
-                    ws_max, gen_arg, spin_ticks, uniform_rows, red, reinterpret_cast<uint32_t*>(stage),
-                    nullptr);
+    dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
+                    ws_max, spin_ticks, uniform_rows, red, reinterpret_cast<uint32_t*>(stage), nullptr);
 }
 
-// Advances the epoch word by one, keeping its top bit set so that epochs
-// never equal a host-chosen generation (top bit clear).
-__global__ void dim0_epoch_bump_kernel(uint32_t* __restrict__ ws_epoch) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        uint32_t n = (*ws_epoch & 0x7FFFFFFFu) + 1u;
-        if (n > 0x7FFFFFFFu) n = 1u;
-        *ws_epoch = 0x80000000u | n;
-    }
+// Zero fill of n 16-byte words (a fresh workspace; no memset node, so the
+// same call also works inside a captured graph).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
                        bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
-                       void* ws, uint32_t gen, long long spin_ticks, hipStream_t stream) {
+                       void* ws, long long spin_ticks, hipStream_t stream) {
     const int64_t chunk_rows = transposed ? kDim0ChunkRowsT : kDim0ChunkRows;
     const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max, lt_cap, chunk_rows);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
     const int64_t grid = n_tiles < kDim0MaxGrid ? n_tiles : kDim0MaxGrid;
     const Dim0Workspace w = dim0_workspace(M, K);
     char* base = static_cast<char*>(ws);
-    const uint32_t* ws_epoch = base ? reinterpret_cast<const uint32_t*>(base + w.epoch_off) : nullptr;
+    uint32_t* ws_ctr = base ? reinterpret_cast<uint32_t*>(base + w.ctr_off) : nullptr;
     uint64_t* ws_max = base ? reinterpret_cast<uint64_t*>(base + w.max_off) : nullptr;
     // a group can need column-maximum tiles only if M rows make more chunks
     // than a team may have
     const int maybe_c = (int64_t)M > chunk_rows * team_max ? 1 : 0;
     hipLaunchKernelGGL(transposed ? dim0t_kernel : dim0_kernel, dim3((unsigned)grid), dim3(kThreads),
                        0, stream, x, M, K, off, G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max,
-                       lt_cap, maybe_c, ws_epoch, ws_max, gen, spin_ticks, uniform_rows);
+                       lt_cap, maybe_c, ws_ctr, ws_max, spin_ticks, uniform_rows);
     return hipGetLastError();
 }
 
-hipError_t launch_dim0_epoch_bump(void* ws, hipStream_t stream) {
-    hipLaunchKernelGGL(dim0_epoch_bump_kernel, dim3(1), dim3(64), 0, stream,
-                       reinterpret_cast<uint32_t*>(static_cast<char*>(ws)));
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+    const int64_t n = (int64_t)(bytes / 16);
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = n / 256 + 1 < 1024 ? n / 256 + 1 : 1024;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<uint4*>(p), n);
     return hipGetLastError();
 }
 

@@ -104,22 +104,28 @@ inline int dim0_lt_cap(int64_t M, int64_t K, int64_t G, int64_t team_max, int64_
     return lt;
 }
 
-// dim0 workspace (needed only when M > kDim0ChunkRowsT), 256-byte aligned
-// regions: an epoch word, then the column maxima of every chunk, one 64-bit
-// word per column pair (generation << 32 | two 16-bit magnitude patterns).
-// Sized for the smaller chunks (dim0_t's), so one workspace serves both
-// kernels.
+// dim0 workspace (needed only when M > kDim0ChunkRowsT), in two 256-byte
+// aligned regions: one 32-bit counter per (chunk row, 128-column strip), then
+// the column maxima of every chunk row, one 64-bit word per column pair
+// (a presence tag in the high half, two 16-bit magnitude patterns in the
+// low half). A team of chunk tiles (one chunked group, one strip) uses the
+// counter at (its first chunk row, its strip) and the words of its chunk rows
+// in its strip. Sized for the smaller chunks (dim0_t's), so one workspace
+// serves both kernels. Zero-filled before first use; every launch leaves it
+// zero-filled again (see mgs_dim0.hip).
 struct Dim0Workspace {
-    int64_t chunks;
-    size_t epoch_off, max_off, bytes;
+    int64_t chunks;      // chunk rows
+    int64_t strips;      // 128-column strips, ceil(K / 128)
+    size_t ctr_off, max_off, bytes;
 };
 
 inline Dim0Workspace dim0_workspace(int64_t M, int64_t K) {
     Dim0Workspace w;
     w.chunks = dim0_chunk_bound(M, kDim0ChunkRowsT);
-    w.epoch_off = 0;
-    w.max_off = 256;
-    w.bytes = w.max_off + (size_t)(w.chunks * (K / 2)) * sizeof(uint64_t);
+    w.strips = (K + 127) / 128;
+    w.ctr_off = 0;
+    w.max_off = ((size_t)(w.chunks * w.strips) * sizeof(uint32_t) + 255) / 256 * 256;
+    w.bytes = w.chunks > 0 ? w.max_off + (size_t)(w.chunks * (K / 2)) * sizeof(uint64_t) : 0;
     return w;
 }
 

@@ -28,6 +28,9 @@
 #include "mgs_device.hpp"
 #include "mgs_kernels.hpp"
 
+#include <map>
+#include <mutex>
+
 namespace mgs {
 
 namespace {
@@ -175,6 +178,37 @@ __global__ __launch_bounds__(1024) void dim1_kernel(
     }
 }
 
+// Workgroups of dim1_kernel<V> resident per CU for a launch shape, from the
+// runtime's occupancy query, kept per (device, threads, LDS bytes): the query
+// costs more than the rest of a call's host work.
+template <int V>
+int resident_per_cu(int threads, size_t shmem) {
+    struct Key {
+        int dev, threads;
+        size_t shmem;
+        bool operator<(const Key& o) const {
+            return dev != o.dev ? dev < o.dev : threads != o.threads ? threads < o.threads : shmem < o.shmem;
+        }
+    };
+    static std::mutex mu;
+    static std::map<Key, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const Key key{dev, threads, shmem};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dim1_kernel<V>, threads, shmem) !=
+            hipSuccess || per_cu < 1)
+        per_cu = 1;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = per_cu;
+    return per_cu;
+}
+
 template <int V>
 hipError_t launch_v(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,
                     uint8_t* q, float* scales, int threads, int cus, hipStream_t stream) {
@@ -183,10 +217,7 @@ hipError_t launch_v(const uint16_t* x, int64_t M, int K, const int32_t* off, int
     // walking M / blocks rows with the next row in flight. A second round
     // (twice the resident count) measured 2 us slower at (8192, 16640):
     // the workgroups that start late finish late.
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dim1_kernel<V>, threads, shmem) !=
-            hipSuccess || per_cu < 1)
-        per_cu = 1;
+    const int per_cu = resident_per_cu<V>(threads, shmem);
     const int64_t resident = (int64_t)per_cu * (cus > 0 ? cus : 1);
     const int64_t blocks = M < resident ? M : resident;
     hipLaunchKernelGGL(dim1_kernel<V>, dim3((unsigned)blocks), dim3(threads), shmem, stream, x, M,

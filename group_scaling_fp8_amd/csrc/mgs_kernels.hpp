@@ -9,21 +9,22 @@
 namespace mgs {
 
 // team_max: the most chunks a group may have to be cast as a team (at most
-// the CU count, see mgs_dim0.hip). gen != 0: the generation number this
-// call's maxima words carry. gen == 0: the generation is read from the
-// workspace's epoch word, which launch_dim0_epoch_bump advances in stream
-// order (for graph replays). spin_ticks bounds a tile's wait for maxima
-// written by other tiles, in device wall-clock ticks; past it the tile
-// computes them itself. A negative value skips the wait.
+// the CU count, see mgs_dim0.hip). ws: the dim0 workspace (Dim0Workspace
+// layout for (M, K), zero-filled; every launch leaves it so), or null when M
+// rows cannot make a chunked group. spin_ticks bounds a tile's wait
+// for maxima written by other tiles, in device wall-clock ticks; past it the
+// tile computes them itself. A negative value skips the wait.
 // lt_cap: the widest strips allowed, 8 << lt_cap columns (dim0_lt_cap).
 // uniform_rows >= 0: G equal groups of that many rows and no offsets array
-// (off unused); -1: group ends from off. transposed: q is (K, M) and scales (K, G) (dim0_t); M and the
-// group ends must then be multiples of 16 (ends are rounded down to them).
+// (off unused); -1: group ends from off. transposed: q is (K, M) and scales
+// (K, G) (dim0_t); M and the group ends must then be multiples of 16 (ends
+// are rounded down to them).
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
                        bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
-                       void* ws, uint32_t gen, long long spin_ticks, hipStream_t stream);
+                       void* ws, long long spin_ticks, hipStream_t stream);
 
-hipError_t launch_dim0_epoch_bump(void* ws, hipStream_t stream);
+// Zero fill of bytes / 16 16-byte words at p (16-byte aligned) by a kernel.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
 // cus: compute units of the device; the grid is the workgroups that fit at once.
 hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,

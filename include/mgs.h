@@ -29,6 +29,12 @@
  *     asynchronous and stream-ordered. Calls are thread-safe.
  *   - Return value: an mgs_status. Argument errors are reported before any
  *     GPU work is queued. MGS_ERR_HIP reports a failed launch or allocation.
+ *   - The library reads no environment variables and never synchronises a
+ *     stream or the device, except under MGS_FLAG_VALIDATE. It allocates
+ *     device memory in one place only: mgs_quant_groups_dim0, and the other
+ *     dim0-family calls when given no workspace, keep a workspace of their
+ *     own (described there). Every other call, and every call given a
+ *     workspace, allocates and frees nothing.
  *   - Numerics: scale = fl32(448 / max(amax, 1e-12)) with one IEEE binary32
  *     division. With MGS_FLAG_POW2_SCALE it is rounded down to a power of
  *     two. q = E4M3(fl32(x * scale)): clamp to [-448, 448], round to
@@ -72,7 +78,7 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * kernel-argument dict of its torch.compile failure report).
  *   x       (M, K) bf16. Groups split the M rows.
  *   offsets n_groups int32 end offsets along M, 1 <= n_groups <= 1024.
- *   flags   0 or MGS_FLAG_POW2_SCALE.
+ *   flags   0, MGS_FLAG_POW2_SCALE, MGS_FLAG_VALIDATE.
  *   q       (M, K) E4M3 bytes, written.
  *   scales  (n_groups, K) fp32, written. scales[g, k] is the multiplier for
  *           column k of group g. An empty group still gets its row, with the
@@ -80,33 +86,71 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * Requirements: M >= 0, K >= 0, K % 8 == 0; x 16-byte aligned, q 8-byte
  * aligned, scales 16-byte aligned. M == 0 writes only the scales; K == 0 is a
  * no-op.
- * Memory: a group taller than 896 rows is cut into chunks of at most 896
- * rows (a tile holds 896 rows of 128 columns: 160 KiB in registers and 64 KiB
- * in LDS). Each chunk's column maxima go through a device workspace
- * of about (M / 320) * K * 4 bytes, between workgroups of the one kernel
- * launch. A tile that waits for other tiles' maxima waits at most about
- * 20 ms of device wall clock; past that it computes them from x itself, so
- * the result never depends on workgroup scheduling. Two environment
- * variables, read on every call, exist for testing:
- *   - MGS_DIM0_SPIN_TICKS sets that bound in wall-clock ticks; a negative
- *     value skips the wait.
- *   - MGS_DIM0_TEAM_MAX lowers the most chunks a group may have and still be
- *     cast by one team of workgroups (default min(128, CU count)); taller
- *     groups read their chunks twice.
- * The library allocates the workspace once per (device, stream)
- * with hipMalloc, zeroes it, grows it as needed, and frees it only at process
- * exit. Graph capture: a call on a capturing stream adds one single-thread
- * kernel before the main one and replays correctly. When M > 640 it needs
- * the workspace to exist already, so make one call of at least that size
- * eagerly on the same stream first. Otherwise it returns
- * MGS_ERR_UNSUPPORTED. Replays use the capturing stream's workspace, so they
- * must not overlap other calls made on that stream.
+ * Tall groups: a group taller than 896 rows is cut into chunks of at most
+ * 896 rows (a tile holds 896 rows of 128 columns: 160 KiB in registers and
+ * 64 KiB in LDS). The chunks' column maxima pass between workgroups of the
+ * one kernel launch through a device workspace of
+ * mgs_dim0_workspace_bytes(M, K) bytes (0 when M <= 640, else about
+ * M * K / 80 bytes). A tile that waits for other tiles' maxima waits at most
+ * about 20 ms of device wall clock; past that it computes them from x
+ * itself, so the result never depends on workgroup scheduling.
+ * Memory: this call takes no workspace argument (its signature is the one
+ * the per-group dim0 cast is known by), so it uses the library's own: one
+ * per (device, stream), allocated with hipMalloc and zero-filled by a kernel
+ * on the stream the first time a call on that stream needs one, and
+ * replaced by a larger one when a later call needs more. Replaced buffers
+ * are kept until process exit (graphs captured earlier may still use them);
+ * nothing is freed and no stream is synchronised. Inside graph capture no
+ * allocation is possible: a capturing call that needs more workspace than
+ * its stream has returns MGS_ERR_UNSUPPORTED. mgs_quant_groups_dim0_ws takes
+ * the workspace from the caller instead and never allocates. Calls sharing a
+ * workspace must not run at the same time (calls on one stream never do).
  * Errors: MGS_ERR_UNSUPPORTED if the tile count bound reaches 2^31.
  */
 int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
                           const int32_t *offsets, int32_t n_groups,
                           uint32_t flags, void *q, float *scales,
                           void *stream);
+
+/*
+ * Size in bytes of the workspace that the dim0-family calls on an (M, K)
+ * input need (mgs_quant_groups_dim0_ws, mgs_quant_groups_dim0_t, and
+ * mgs_quant_experts_dim1 with M = E * D1, K = D2): 0 when M <= 640 (no group
+ * can be cut into chunks), else, with c = M / 640 + M / 641 chunk rows,
+ * round_up(4 * c * ceil(K / 128), 256) + 8 * c * (K / 2).
+ * Host only; no GPU work. Returns MGS_ERR_INVALID_ARG for a null `bytes` or
+ * negative sizes, MGS_ERR_UNSUPPORTED for M or K over 2^31 - 1.
+ */
+int mgs_dim0_workspace_bytes(int64_t M, int64_t K, int64_t *bytes);
+
+/*
+ * mgs_quant_groups_dim0 with a workspace owned by the caller, the form that
+ * leaves every allocation to the caller ([BLOCKSIZE] torch.compile failure
+ * report: the kernel writes caller-provided outputs in place, and its
+ * constants are launch parameters).
+ *   workspace        device memory of at least mgs_dim0_workspace_bytes(M, K)
+ *                    bytes, 256-byte aligned, zero-filled by the caller
+ *                    before its first use. Every call leaves it zero-filled
+ *                    again (each team of workgroups clears the counter and
+ *                    the column maxima it used), so it needs no clearing
+ *                    between calls and serves calls of any shape that fits
+ *                    it. Two calls that may run at the same time (on
+ *                    different streams) need two workspaces. NULL with
+ *                    workspace_bytes 0 selects the library's own workspace
+ *                    (exactly mgs_quant_groups_dim0). When the required size
+ *                    is 0 the workspace is not touched.
+ *   workspace_bytes  its size.
+ * Never allocates, frees or synchronises (MGS_FLAG_VALIDATE aside), so it
+ * can be captured into a graph on any stream.
+ * Errors: as mgs_quant_groups_dim0, plus MGS_ERR_INVALID_ARG for a workspace
+ * that is misaligned or smaller than required, or a NULL workspace with a
+ * nonzero size.
+ */
+int mgs_quant_groups_dim0_ws(const void *x, int64_t M, int64_t K,
+                             const int32_t *offsets, int32_t n_groups,
+                             uint32_t flags, void *q, float *scales,
+                             void *workspace, int64_t workspace_bytes,
+                             void *stream);
 
 /*
  * Per-group scaling along dim0 with transposed outputs ([ROWWISE] Summary:
@@ -126,16 +170,19 @@ int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
  *   q_t      (K, M) E4M3 bytes, written: q_t[k, r] = dim0's q[r, k].
  *   scales_t (K, n_groups) fp32, written: scales_t[k, g] = dim0's
  *            scales[g, k]; empty groups get the amax = 0 value.
+ *   workspace, workspace_bytes  as for mgs_quant_groups_dim0_ws (NULL, 0:
+ *            the library's own workspace).
  * Requirements: M % 16 == 0, K % 8 == 0; x and q_t 16-byte aligned,
  * scales_t 4-byte aligned. M == 0 writes only the scales; K == 0 is a
- * no-op. Memory, the bounded wait, graph capture and errors are as for
- * mgs_quant_groups_dim0, except that tiles hold 640 rows of 128 columns (all
- * in registers: LDS holds the transposed output stage), so groups taller than
- * 640 rows are cut into chunks of at most 640 rows.
+ * no-op. The bounded wait and errors are as for mgs_quant_groups_dim0_ws,
+ * except that tiles hold 640 rows of 128 columns (all in registers: LDS
+ * holds the transposed output stage), so groups taller than 640 rows are cut
+ * into chunks of at most 640 rows.
  */
 int mgs_quant_groups_dim0_t(const void *x, int64_t M, int64_t K,
                             const int32_t *offsets, int32_t n_groups,
                             uint32_t flags, void *q_t, float *scales_t,
+                            void *workspace, int64_t workspace_bytes,
                             void *stream);
 
 /*
@@ -150,13 +197,17 @@ int mgs_quant_groups_dim0_t(const void *x, int64_t M, int64_t K,
  *           has nothing to check).
  *   q       (E, D1, D2) E4M3 bytes, written.
  *   scales  (E, D2) fp32, written.
+ *   workspace, workspace_bytes  as for mgs_quant_groups_dim0_ws with
+ *           M = E * D1, K = D2 (NULL, 0: the library's own workspace).
  * Requirements: 1 <= E <= 1024, D1 >= 0, E * D1 < 2^31, D2 % 8 == 0; w
  * 16-byte aligned, q 8-byte aligned, scales 16-byte aligned. Experts taller
- * than 896 rows are cut into chunks exactly as dim0's groups (workspace,
- * bounded wait and graph capture as for mgs_quant_groups_dim0).
+ * than 896 rows are cut into chunks exactly as dim0's groups (bounded wait
+ * and errors as for mgs_quant_groups_dim0_ws).
  */
 int mgs_quant_experts_dim1(const void *w, int64_t E, int64_t D1, int64_t D2,
-                           uint32_t flags, void *q, float *scales, void *stream);
+                           uint32_t flags, void *q, float *scales,
+                           void *workspace, int64_t workspace_bytes,
+                           void *stream);
 
 /*
  * Per-group rowwise scaling along dim1 ([ROWWISE] Summary).
@@ -196,13 +247,6 @@ int mgs_mx_quant_dim0(const void *x, int64_t M, int64_t K,
                       void *q, uint8_t *scales_e8m0, void *stream);
 
 /*
- * The library's own E4M3 cast on its own: out[i] = E4M3(clamp(in[i])), the
- * last step of every entry point above, exposed so it can be checked over
- * 2^32 binary32 inputs. in: n fp32 values, out: n bytes (device). +-Inf
- * saturate to 0x7E / 0xFE; NaN inputs are outside the contract.
- * Requirements: n % 4 == 0, in 16-byte aligned, out 4-byte aligned.
- */
-/*
  * MX-style block-32 cast along dim0, written transposed (the dim1 form of
  * [MXA2A]'s cast benchmark modes: blocks of 32 consecutive rows of one
  * column). The values are mgs_mx_quant_dim0's on x^T, computed from x in
@@ -212,8 +256,7 @@ int mgs_mx_quant_dim0(const void *x, int64_t M, int64_t K,
  *   q_t       (K, M) E4M3 bytes: q_t[k, r] is x[r, k] cast with the scale
  *             of rows 32 * (r / 32) .. + 31 of column k.
  *   scales_t  (K, M/32) bytes, E8M0 (exponent + 127).
- * Requirements: x 16-byte aligned, q_t 8-byte aligned. M == 0 or K == 0 is
- * a no-op.
+ * Requirements: x and q_t 16-byte aligned. M == 0 or K == 0 is a no-op.
  */
 int mgs_mx_quant_dim1(const void *x, int64_t M, int64_t K, int mode,
                       void *q_t, uint8_t *scales_t, void *stream);
@@ -232,6 +275,13 @@ int mgs_mx_quant_dim1(const void *x, int64_t M, int64_t K, int mode,
 int mgs_mx_dequant_dim0(const void *q, const uint8_t *scales_e8m0, int64_t M,
                         int64_t K, void *y, void *stream);
 
+/*
+ * The library's own E4M3 cast on its own: out[i] = E4M3(clamp(in[i])), the
+ * last step of every entry point above, exposed so it can be checked over
+ * 2^32 binary32 inputs. in: n fp32 values, out: n bytes (device). +-Inf
+ * saturate to 0x7E / 0xFE; NaN inputs are outside the contract.
+ * Requirements: n % 4 == 0, in 16-byte aligned, out 4-byte aligned.
+ */
 int mgs_cast_e4m3(const float *in, int64_t n, uint8_t *out, void *stream);
 
 /*
@@ -240,6 +290,31 @@ int mgs_cast_e4m3(const float *in, int64_t n, uint8_t *out, void *stream);
  * against a kernel of known size.
  */
 int mgs_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+/*
+ * TEST ONLY (not part of the product interface): the dim0-family cast with
+ * two launch parameters overridden, so tests can reach paths that the
+ * defaults reach only under rare scheduling.
+ *   uniform_rows  -1: groups from offsets (mgs_quant_groups_dim0_ws, or
+ *                 mgs_quant_groups_dim0_t when transposed != 0); >= 0:
+ *                 n_groups equal groups of that many rows and no offsets
+ *                 (mgs_quant_experts_dim1 with E = n_groups, D1 =
+ *                 uniform_rows; M must be E * D1, transposed must be 0).
+ *   spin_ticks    bound on a tile's wait for other tiles' column maxima, in
+ *                 device wall-clock ticks; -1 skips the wait (the waiting
+ *                 tile computes the maxima from x); below -1: the default.
+ *   team_max      1 up to the library's limit lowers the most chunks a group
+ *                 may have and still be cast by one team of workgroups
+ *                 (taller groups then read their chunks twice); other
+ *                 values: the default.
+ * Every other argument is as for the call it stands for.
+ */
+int mgs_test_quant_dim0(const void *x, int64_t M, int64_t K,
+                        const int32_t *offsets, int32_t n_groups,
+                        int64_t uniform_rows, uint32_t flags, int transposed,
+                        void *q, float *scales, void *workspace,
+                        int64_t workspace_bytes, int64_t spin_ticks,
+                        int32_t team_max, void *stream);
 
 /* Static text for a status code. */
 const char *mgs_status_string(int status);

@@ -44,14 +44,18 @@ def test_status_strings(L):
     assert L.mgs_status_string(99) == b"unknown status"
 
 
-@pytest.mark.parametrize("fn", ["mgs_quant_groups_dim0", "mgs_quant_groups_dim0_t",
-                                "mgs_quant_groups_dim1"])
+@pytest.mark.parametrize("fn", ["mgs_quant_groups_dim0", "mgs_quant_groups_dim0_ws",
+                                "mgs_quant_groups_dim0_t", "mgs_quant_groups_dim1"])
 def test_grouped_argument_errors(L, fn):
     f = getattr(L, fn)
-    ok = dict(x=A, M=64, K=128, off=A, G=4, flags=0, q=A, s=A, stream=None)
+    ok = dict(x=A, M=64, K=128, off=A, G=4, flags=0, q=A, s=A, ws=None, wsb=0, stream=None)
+    takes_ws = fn.endswith("_ws") or fn.endswith("_t")
 
     def call(**kw):
         a = dict(ok, **kw)
+        if takes_ws:
+            return f(a["x"], a["M"], a["K"], a["off"], a["G"], a["flags"], a["q"], a["s"], a["ws"],
+                     a["wsb"], a["stream"])
         return f(a["x"], a["M"], a["K"], a["off"], a["G"], a["flags"], a["q"], a["s"], a["stream"])
 
     assert call(M=-1) == INVALID
@@ -69,7 +73,16 @@ def test_grouped_argument_errors(L, fn):
     assert call(q=A + 4) == INVALID
     assert call(s=None) == INVALID
     assert call(M=1 << 31) == UNSUPPORTED
-    if fn.endswith("dim0"):
+    if takes_ws:
+        assert call(ws=None, wsb=256) == INVALID          # a size without a buffer
+        assert call(ws=A + 128, wsb=1 << 20) == INVALID   # 256-byte alignment
+        assert call(ws=A, wsb=-1) == INVALID
+        # M = 2000 rows can make chunked groups: the workspace must be big enough
+        need = ctypes.c_int64(0)
+        assert L.mgs_dim0_workspace_bytes(2000, 128, ctypes.byref(need)) == mgs.MGS_OK
+        assert need.value > 0
+        assert call(M=2000, ws=A, wsb=need.value - 8) == INVALID
+    if fn.endswith("dim0") or fn.endswith("dim0_ws"):
         assert call(K=12) == INVALID
         assert call(s=A + 4) == INVALID
         # 1024 groups of 1024-column strips over K = 2^31 - 8: the tile bound reaches 2^31
@@ -87,17 +100,60 @@ def test_grouped_argument_errors(L, fn):
 
 
 def test_experts_argument_errors(L):
-    f = L.mgs_quant_experts_dim1
-    assert f(A, 0, 64, 128, 0, A, A, None) == INVALID        # E >= 1
-    assert f(A, 2, -1, 128, 0, A, A, None) == INVALID
-    assert f(A, 1025, 16, 128, 0, A, A, None) == UNSUPPORTED
-    assert f(A, 4, 1 << 30, 128, 0, A, A, None) == UNSUPPORTED   # E * D1 >= 2^31
-    assert f(A, 2, 64, 12, 0, A, A, None) == INVALID         # D2 % 8
-    assert f(A, 2, 64, 128, 4, A, A, None) == INVALID        # unknown flag
-    assert f(A + 8, 2, 64, 128, 0, A, A, None) == INVALID
-    assert f(A, 2, 64, 128, 0, A + 4, A, None) == INVALID
-    assert f(A, 2, 64, 128, 0, A, A + 4, None) == INVALID
-    assert f(None, 2, 64, 128, 0, A, A, None) == INVALID
+    def f(*a):
+        return L.mgs_quant_experts_dim1(*a[:7], None, 0, None)
+    assert f(A, 0, 64, 128, 0, A, A) == INVALID        # E >= 1
+    assert f(A, 2, -1, 128, 0, A, A) == INVALID
+    assert f(A, 1025, 16, 128, 0, A, A) == UNSUPPORTED
+    assert f(A, 4, 1 << 30, 128, 0, A, A) == UNSUPPORTED   # E * D1 >= 2^31
+    assert f(A, 2, 64, 12, 0, A, A) == INVALID         # D2 % 8
+    assert f(A, 2, 64, 128, 4, A, A) == INVALID        # unknown flag
+    assert f(A + 8, 2, 64, 128, 0, A, A) == INVALID
+    assert f(A, 2, 64, 128, 0, A + 4, A) == INVALID
+    assert f(A, 2, 64, 128, 0, A, A + 4) == INVALID
+    assert f(None, 2, 64, 128, 0, A, A) == INVALID
+    # 2 experts of 1000 rows need a workspace; a short one is refused
+    assert L.mgs_quant_experts_dim1(A, 2, 1000, 128, 0, A, A, A, 256, None) == INVALID
+
+
+def test_workspace_size_query(L):
+    n = ctypes.c_int64(-1)
+    assert L.mgs_dim0_workspace_bytes(640, 4096, ctypes.byref(n)) == mgs.MGS_OK and n.value == 0
+    def expect(M, K):
+        c = M // 640 + M // 641
+        return -(-4 * c * -(-K // 128) // 256) * 256 + 8 * c * (K // 2)
+    assert L.mgs_dim0_workspace_bytes(641, 8, ctypes.byref(n)) == mgs.MGS_OK
+    assert n.value == expect(641, 8) == 256 + 8 * 2 * 4
+    assert L.mgs_dim0_workspace_bytes(16640, 8192, ctypes.byref(n)) == mgs.MGS_OK
+    assert n.value == expect(16640, 8192)
+    assert L.mgs_dim0_workspace_bytes(-1, 8, ctypes.byref(n)) == INVALID
+    assert L.mgs_dim0_workspace_bytes(8, 8, None) == INVALID
+    assert L.mgs_dim0_workspace_bytes(1 << 31, 8, ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_test_entry_argument_errors(L):
+    f = L.mgs_test_quant_dim0
+    # equal groups: M must be n_groups * uniform_rows, and no transposed form
+    assert f(A, 300, 64, None, 3, 100, 0, 1, A, A, None, 0, -2, 0, None) == INVALID
+    assert f(A, 301, 64, None, 3, 100, 0, 0, A, A, None, 0, -2, 0, None) == INVALID
+    assert f(A, 64, 128, A, 4, -1, 8, 0, A, A, None, 0, -2, 0, None) == INVALID
+
+
+def _undefined_symbols(path):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+
+
+def test_library_reads_no_environment(L):
+    """The library takes every setting as an argument: it imports no
+    environment reader."""
+    und = _undefined_symbols(mgs.library_path())
+    assert not und & {"getenv", "secure_getenv", "__secure_getenv", "environ"}, und
+    # the only allocation and the only stream wait it may make: the own
+    # workspace of calls given none, and MGS_FLAG_VALIDATE's offsets copy
+    assert "hipFree" not in und and "hipDeviceSynchronize" not in und
 
 
 def test_mx_dim1_argument_errors(L):
@@ -107,6 +163,7 @@ def test_mx_dim1_argument_errors(L):
     assert f(A, 64, 64, 2, A, A, None) == INVALID           # mode
     assert f(A + 8, 64, 64, 0, A, A, None) == INVALID
     assert f(A, 64, 64, 0, A + 4, A, None) == INVALID
+    assert f(A, 64, 64, 0, A + 8, A, None) == INVALID       # q_t takes 16-byte stores
     assert f(A, 64, 64, 0, A, None, None) == INVALID
     assert f(A, 0, 64, 0, A, A, None) == mgs.MGS_OK
 

@@ -3,7 +3,7 @@ q_t (K, M) and scales_t (K, G) against the oracle byte for byte, over every
 strip class (1024- down to 128-column strips, K narrower than a strip,
 ragged last strips), empty groups, chunk teams and column-maximum tiles,
 the path that computes the maxima in the waiting tile itself, pow2 scales,
-the benchmark shape on sampled columns, and offsets that are not multiples
+the benchmark shape compared whole, and offsets that are not multiples
 of 16 (values unspecified, writes in bounds). Every output carries guard
 bands."""
 import numpy as np
@@ -14,6 +14,7 @@ import oracle
 import group_scaling_fp8_amd as mgs
 from group_scaling_fp8_amd import workloads as wl
 from gpu_util import Guarded, assert_same_bytes, to_dev
+from oracle_pool import check_dim0_t_whole
 
 pytestmark = pytest.mark.gpu
 
@@ -70,23 +71,31 @@ def test_dim0_t_no_rows_writes_scales():
     assert_same_bytes(s, rs, "scales_t of empty groups")
 
 
-@pytest.mark.parametrize("team_max,spin", [("1", None), (None, "-1")])
-def test_dim0_t_tall_groups_other_paths(team_max, spin, monkeypatch):
-    # column-maximum tiles (team limit 1), then the in-tile fallback (no wait)
-    if team_max:
-        monkeypatch.setenv("MGS_DIM0_TEAM_MAX", team_max)
-    if spin:
-        monkeypatch.setenv("MGS_DIM0_SPIN_TICKS", spin)
+@pytest.mark.parametrize("team_max,spin", [(1, mgs.api.TEST_DEFAULT_SPIN),
+                                           (mgs.api.TEST_DEFAULT_TEAM, -1)])
+def test_dim0_t_tall_groups_other_paths(team_max, spin):
+    # column-maximum tiles (team limit 1), then the in-tile fallback (no wait),
+    # through the test-only entry point
     sizes = [1296, 16, 2000]
     off = np.cumsum(sizes).astype(np.int32)
-    check(data(5, int(off[-1]), 136), off, "tall groups team_max=%s spin=%s" % (team_max, spin))
+    x = data(5, int(off[-1]), 136)
+    M, K = x.shape
+    gq, gs = Guarded((K, M), torch.uint8), Guarded((K, len(off)), torch.float32)
+    mgs.api._test_quant_dim0(to_dev(x), to_dev(off), gq.view, gs.view, transposed=True,
+                             spin_ticks=spin, team_max=team_max, workspace=mgs.dim0_workspace(M, K))
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    rq, rs = oracle.quant_groups_dim0_t(x, off)
+    what = "tall groups team_max=%s spin=%s" % (team_max, spin)
+    assert_same_bytes(gs.numpy(), rs, what + " scales_t")
+    assert_same_bytes(gq.numpy(), rq, what + " q_t")
 
 
-def test_dim0_t_matches_dim0_at_the_benchmark_shape():
-    """(16640, 8192) G=64, the benchmark's offsets: q_t and scales_t are dim0's
-    outputs transposed (GPU against GPU, every byte), and sampled columns
-    match the oracle."""
-    T = wl.token_major_gradient()
+def test_dim0_t_at_the_benchmark_shape_whole(token_major):
+    """(16640, 8192) G=64, the benchmark's offsets: every byte of q_t and
+    every scale against the oracle, and against dim0's outputs transposed."""
+    T = token_major
     off = wl.target_offsets(64)
     xt, ot = to_dev(T), to_dev(off)
     q0, s0 = mgs.mgs_quant_groups_dim0(xt, ot)
@@ -94,10 +103,7 @@ def test_dim0_t_matches_dim0_at_the_benchmark_shape():
     torch.cuda.synchronize()
     assert torch.equal(qt, q0.t().contiguous()), "q_t differs from dim0's q transposed"
     assert torch.equal(st.view(torch.int32), s0.t().contiguous().view(torch.int32))
-    cols = np.random.default_rng(9).choice(T.shape[1], 24, replace=False)
-    rq, rs = oracle.quant_groups_dim0_t(np.ascontiguousarray(T[:, cols]), off)
-    assert_same_bytes(qt[torch.from_numpy(cols).to(qt.device)].cpu().numpy(), rq, "sampled q_t rows")
-    assert_same_bytes(st[torch.from_numpy(cols).to(st.device)].cpu().numpy(), rs, "sampled scales_t rows")
+    check_dim0_t_whole(T, off, False, qt.cpu().numpy(), st.cpu().numpy(), "dim0_t (16640, 8192) G=64")
 
 
 def test_dim0_t_unaligned_offsets_stay_in_bounds():

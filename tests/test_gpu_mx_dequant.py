@@ -1,7 +1,7 @@
 """GPU parity of the MX dequantisation (mgs_mx_dequant_dim0) against the
 oracle, bit for bit: every (E4M3 code, E8M0 byte) pair, the round trip of
 the MX configuration's shape (the library's own quantisation, then its
-dequantisation, on sampled rows against the oracle's dequantisation of the
+dequantisation, every value against the oracle's dequantisation of the
 same bytes), a ragged flat tail, and guard bands on the output."""
 import numpy as np
 import pytest
@@ -11,6 +11,7 @@ import oracle
 import group_scaling_fp8_amd as mgs
 from group_scaling_fp8_amd import workloads as wl
 from gpu_util import Guarded, assert_same_bytes, to_dev
+from oracle_pool import check_mx_dequant_whole
 
 pytestmark = pytest.mark.gpu
 
@@ -46,18 +47,14 @@ def test_random_bytes_ragged(M, K):
 
 
 @pytest.mark.parametrize("mode", [mgs.MGS_MX_FLOOR, mgs.MGS_MX_RCEIL])
-def test_round_trip_at_the_mx_shape(mode):
-    c5 = wl.c5_mx()
+def test_round_trip_at_the_mx_shape(c5, mode):
+    """The library's quantisation of the MX configuration, then its
+    dequantisation: every bf16 of y against the oracle's dequantisation of
+    the same bytes (the quantisation itself is compared whole in
+    test_gpu_parity.py)."""
     x = to_dev(c5.x)
     q, s = mgs.mgs_mx_quant_dim0(x, mode)
     y = mgs.mgs_mx_dequant_dim0(q, s)
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(5 + mode).choice(c5.x.shape[0], 48, replace=False))
-    ri = torch.from_numpy(rows).to(q.device)
-    qs, ss = q[ri].cpu().numpy(), s[ri].cpu().numpy()
-    got = y[ri].view(torch.int16).cpu().numpy().view(np.uint16)
-    assert_same_bytes(got, oracle.mx_dequant_dim0(qs, ss), "dequantised sampled rows")
-    # and the quantisation itself on those rows, against the oracle's
-    rq, rs = oracle.mx_quant_dim0(c5.x[rows], mode)
-    assert_same_bytes(qs, rq, "quantised sampled rows")
-    assert_same_bytes(ss, rs, "scales of sampled rows")
+    check_mx_dequant_whole(q.cpu().numpy(), s.cpu().numpy(),
+                           y.view(torch.int16).cpu().numpy().view(np.uint16), "mx round trip")

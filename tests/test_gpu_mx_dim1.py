@@ -1,7 +1,7 @@
 """GPU parity of the MX cast along dim0 with transposed outputs
 (mgs_mx_quant_dim1) against the oracle, bit for bit: ragged tiles in both
 dims, FLOOR and RCEIL, subnormal and zero blocks, and the MX configuration's
-shape on sampled columns. Guard bands on both outputs."""
+shape compared whole. Guard bands on both outputs."""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +10,7 @@ import oracle
 import group_scaling_fp8_amd as mgs
 from group_scaling_fp8_amd import workloads as wl
 from gpu_util import Guarded, assert_same_bytes, to_dev
+from oracle_pool import check_mx_dim1_whole
 
 pytestmark = pytest.mark.gpu
 
@@ -46,12 +47,7 @@ def test_mx_dim1(M, K, mode):
 
 
 @pytest.mark.parametrize("mode", [mgs.MGS_MX_FLOOR, mgs.MGS_MX_RCEIL])
-def test_mx_dim1_at_the_mx_shape(mode):
-    c5 = wl.c5_mx()
+def test_mx_dim1_at_the_mx_shape_whole(c5, mode):
     q, s = mgs.mgs_mx_quant_dim1(to_dev(c5.x), mode)
     torch.cuda.synchronize()
-    cols = np.sort(np.random.default_rng(8 + mode).choice(c5.x.shape[1], 12, replace=False))
-    rq, rs = oracle.mx_quant_dim1(np.ascontiguousarray(c5.x[:, cols]), mode)
-    ci = torch.from_numpy(cols).to(q.device)
-    assert_same_bytes(q[ci].cpu().numpy(), rq, "sampled q_t rows")
-    assert_same_bytes(s[ci].cpu().numpy(), rs, "sampled scales_t rows")
+    check_mx_dim1_whole(c5.x, mode, q.cpu().numpy(), s.cpu().numpy(), "mx dim1 mode %d" % mode)

@@ -1,11 +1,10 @@
 """GPU parity: the HIP path against the CPU oracle, byte for byte.
 
 Tolerance is zero: E4M3 bytes, fp32 scale bits and E8M0 bytes must be
-identical. Small workloads are compared whole; the full-size workloads
-(benchmark shapes, same launch configuration) are compared on sampled
-columns (dim0: every output of a column depends only on that column) or
-sampled rows (dim1, MX: rows are independent), for which the oracle runs on
-exactly the sampled slice of the same input bytes.
+identical. Every configuration is compared whole, at its full size and in
+the launch configuration the benchmark uses; for the large ones the oracle
+runs on independent slices of the same input bytes in a thread pool
+(tests/oracle_pool.py: column slices for dim0, row slices for dim1 and MX).
 Every output buffer carries guard bands that must stay untouched.
 """
 import concurrent.futures as cf
@@ -18,6 +17,7 @@ import oracle
 import group_scaling_fp8_amd as mgs
 from group_scaling_fp8_amd import workloads as wl
 from gpu_util import Guarded, assert_same_bytes, to_dev
+from oracle_pool import check_dim0_whole, check_dim1_whole, check_mx_whole
 
 pytestmark = pytest.mark.gpu
 
@@ -125,67 +125,36 @@ def test_dim0_c2_pow2_empty_and_zero_groups():
     check_dim0(w.x, w.offsets, w.pow2, w.name)
 
 
-def sampled_columns(K, n_strips=3, rng_seed=0):
-    """Whole 128-column strips (first, last, and random ones)."""
-    rng = np.random.default_rng(rng_seed)
-    strips = sorted(set([0, K // 128 - 1] + list(rng.integers(0, K // 128, n_strips))))
-    return np.concatenate([np.arange(s * 128, s * 128 + 128) for s in strips])
-
-
-def check_dim0_sampled(w, cols):
-    q, s = gpu_dim0(w.x, w.offsets, w.pow2)
-    xs = np.ascontiguousarray(w.x[:, cols])
-    rq, rs = oracle.quant_groups_dim0(xs, w.offsets, w.pow2)
-    assert_same_bytes(s[:, cols], rs, w.name + " scales")
-    assert_same_bytes(q[:, cols], rq, w.name + " q")
-
-
-def test_dim0_c3_dirichlet_sampled():
+def test_dim0_c3_dirichlet_whole():
     w = wl.c3_dim0_large()
-    assert wl.sizes_from_offsets(w.offsets).max() > 512     # exercises tall groups
-    check_dim0_sampled(w, sampled_columns(w.x.shape[1]))
+    assert wl.sizes_from_offsets(w.offsets).max() > 896      # exercises chunked groups
+    q, s = gpu_dim0(w.x, w.offsets, w.pow2)
+    check_dim0_whole(w.x, w.offsets, w.pow2, q, s, w.name)
 
 
-@pytest.fixture(scope="module")
-def token_major():
-    return wl.token_major_gradient()
-
-
-def test_dim0_c6_target_sampled(token_major):
+def test_dim0_c6_target_whole(token_major):
     w = wl.c6_dim0_target(64, token_major)
-    check_dim0_sampled(w, sampled_columns(w.x.shape[1], 4))
+    q, s = gpu_dim0(w.x, w.offsets, w.pow2)
+    check_dim0_whole(w.x, w.offsets, w.pow2, q, s, w.name)
 
 
 # ---------------------------------------------------------------- dim1
 
 
 @pytest.mark.parametrize("G", [1, 16, 64])
-def test_dim1_c4_sampled(token_major, G):
+def test_dim1_c4_whole(token_major, G):
     w = wl.c4_dim1(G, token_major)
     q, s = gpu_dim1(w.x, w.offsets)
-    rng = np.random.default_rng(G)
-    rows = np.unique(np.concatenate([[0, w.x.shape[0] - 1], rng.integers(0, w.x.shape[0], 96)]))
-    rq, rs = oracle.quant_groups_dim1(np.ascontiguousarray(w.x[rows]), w.offsets)
-    assert_same_bytes(s[rows], rs, w.name + " scales")
-    assert_same_bytes(q[rows], rq, w.name + " q")
+    check_dim1_whole(w.x, w.offsets, False, q, s, w.name)
 
 
 # ------------------------------------------------------------------ MX
 
 
-@pytest.fixture(scope="module")
-def c5():
-    return wl.c5_mx()
-
-
 @pytest.mark.parametrize("mode", [mgs.MGS_MX_FLOOR, mgs.MGS_MX_RCEIL])
-def test_mx_c5_sampled(c5, mode):
+def test_mx_c5_whole(c5, mode):
     q, s = gpu_mx(c5.x, mode)
-    rng = np.random.default_rng(5 + mode)
-    rows = np.unique(np.concatenate([[0, c5.x.shape[0] - 1], rng.integers(0, c5.x.shape[0], 512)]))
-    rq, rs = oracle.mx_quant_dim0(np.ascontiguousarray(c5.x[rows]), mode)
-    assert_same_bytes(s[rows], rs, "mx scales")
-    assert_same_bytes(q[rows], rq, "mx q")
+    check_mx_whole(c5.x, mode, q, s, "mx mode %d" % mode)
 
 
 # --------------------------------------------------------------- edges
