@@ -16,5 +16,5 @@ from ._lib import (  # noqa: F401
 from .api import (  # noqa: F401
     dim0_workspace, mgs_cast_e4m3, mgs_copy, mgs_dim0_workspace_bytes, mgs_mx_dequant_dim0,
     mgs_mx_quant_dim0, mgs_mx_quant_dim1, mgs_quant_experts_dim1, mgs_quant_groups_dim0,
-    mgs_quant_groups_dim0_t, mgs_quant_groups_dim1,
+    mgs_quant_groups_dim0_noalloc, mgs_quant_groups_dim0_t, mgs_quant_groups_dim1,
 )

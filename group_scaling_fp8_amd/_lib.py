@@ -18,9 +18,11 @@ MGS_MX_FLOOR = 0
 MGS_MX_RCEIL = 1
 MGS_MAX_GROUPS = 1024
 MGS_DIM1_MAX_K = 131072
+MGS_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "mgs_quant_groups_dim0", "mgs_dim0_workspace_bytes", "mgs_quant_groups_dim0_ws",
+    "mgs_quant_groups_dim0_noalloc",
     "mgs_quant_groups_dim0_t", "mgs_quant_experts_dim1",
     "mgs_quant_groups_dim1", "mgs_mx_quant_dim0",
     "mgs_mx_quant_dim1", "mgs_mx_dequant_dim0", "mgs_cast_e4m3",
@@ -55,7 +57,7 @@ def lib():
                 "g.build()'` or `python group_scaling_fp8_amd/build.py`" % _LIB_PATH)
         L = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
-        for name in ("mgs_quant_groups_dim0", "mgs_quant_groups_dim1"):
+        for name in ("mgs_quant_groups_dim0", "mgs_quant_groups_dim0_noalloc", "mgs_quant_groups_dim1"):
             fn = getattr(L, name)
             fn.argtypes = [vp, i64, i64, vp, i32, u32, vp, vp, vp]
             fn.restype = ctypes.c_int

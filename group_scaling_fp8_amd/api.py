@@ -103,6 +103,26 @@ def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = F
     return q, scales
 
 
+def mgs_quant_groups_dim0_noalloc(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
+                                  q: Optional[torch.Tensor] = None,
+                                  scales: Optional[torch.Tensor] = None, stream=None,
+                                  validate: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mgs_quant_groups_dim0 on the library's fixed per-device scratch array:
+    no device memory is allocated (pass q and scales to allocate nothing on
+    the Python side either)."""
+    _need(x, "x", _BF16_LIKE, 2)
+    _need(offsets, "offsets", (torch.int32,), 1)
+    M, K = x.shape
+    G = offsets.shape[0]
+    q = _out(q, (M, K), torch.uint8, x.device, "q")
+    scales = _out(scales, (G, K), torch.float32, x.device, "scales")
+    st = lib().mgs_quant_groups_dim0_noalloc(x.data_ptr(), M, K, offsets.data_ptr(), G,
+                                             _flags(pow2, validate), q.data_ptr(),
+                                             scales.data_ptr(), _stream_handle(stream))
+    check("mgs_quant_groups_dim0_noalloc", st)
+    return q, scales
+
+
 def mgs_quant_groups_dim0_t(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False,
                             q_t: Optional[torch.Tensor] = None,
                             scales_t: Optional[torch.Tensor] = None, stream=None,

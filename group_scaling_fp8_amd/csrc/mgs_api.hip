@@ -148,13 +148,55 @@ struct Dim0Knobs {
     int team_max;           // 1 .. the device's limit lowers it (taller groups go to class C); else the default
 };
 
+// The dim0 workspace of mgs_quant_groups_dim0_noalloc: a fixed array in the
+// code object, one copy per device, alive until the process ends. In host
+// code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to a kernel.
+constexpr size_t kScratchBytes = size_t(MGS_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / sizeof(uint64_t)];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+bool g_scratch_cleared[kMaxDevices];
+
+// This device's copy of scratch, cleared in stream order the first time an
+// eager call needs it. A call being captured before that also queues the
+// clear (into its graph, so every replay starts from a clear array) without
+// counting it as done, since the graph may never run.
+hipError_t device_scratch(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    if (!g_scratch_cleared[dev]) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess) return e;
+        e = launch_zero(g_scratch_ptr[dev], kScratchBytes, stream);
+        if (e != hipSuccess) return e;
+        if (cap == hipStreamCaptureStatusNone) g_scratch_cleared[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 // Every dim0-family entry point: q (M, K) and scales (G, K), or their
 // transposes. uniform_rows >= 0: n_groups equal groups of uniform_rows rows
-// and no offsets. ws == null && ws_bytes == 0: the library's own workspace.
+// and no offsets. ws == null && ws_bytes == 0: the library's own workspace
+// (use_scratch: the static scratch instead, never an allocation).
 int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,
                       int32_t n_groups, uint32_t flags, void* q, float* scales, void* ws,
                       int64_t ws_bytes, void* stream, bool transposed, int64_t uniform_rows,
-                      const Dim0Knobs* knobs) {
+                      const Dim0Knobs* knobs, bool use_scratch = false) {
     const bool uniform = uniform_rows >= 0;
     int st = check_grouped(x, M, K, uniform ? kNoOffsets : offsets, n_groups, flags, q, scales);
     if (st != MGS_OK) return st;
@@ -165,6 +207,7 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
     if (!scales || !aligned(scales, transposed ? 4 : 16)) return MGS_ERR_INVALID_ARG;
     const mgs::Dim0Workspace layout = mgs::dim0_workspace(M, K);
     if (ws && (size_t)ws_bytes < layout.bytes) return MGS_ERR_INVALID_ARG;
+    if (use_scratch && layout.bytes > kScratchBytes) return MGS_ERR_UNSUPPORTED;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((flags & MGS_FLAG_VALIDATE) && !uniform) {
         st = validate_offsets(offsets, n_groups, M, transposed ? 16 : 1, s);
@@ -184,6 +227,9 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
     void* w = ws;
     if (layout.bytes == 0) {
         w = nullptr;            // no chunked group possible: the kernels never touch it
+    } else if (use_scratch) {
+        hipError_t e = device_scratch(s, &w);
+        if (e != hipSuccess) return hip_status(e);
     } else if (!w) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         hipError_t e = hipStreamIsCapturing(s, &cap);
@@ -244,6 +290,13 @@ int mgs_quant_experts_dim1(const void* w, int64_t E, int64_t D1, int64_t D2, uin
                            void* stream) {
     return mgs::quant_experts(w, E, D1, D2, flags, q, scales, workspace, workspace_bytes, stream,
                               nullptr);
+}
+
+int mgs_quant_groups_dim0_noalloc(const void* x, int64_t M, int64_t K, const int32_t* offsets,
+                                  int32_t n_groups, uint32_t flags, void* q, float* scales,
+                                  void* stream) {
+    return mgs::quant_groups_dim0(x, M, K, offsets, n_groups, flags, q, scales, nullptr, 0, stream,
+                                  false, -1, nullptr, true);
 }
 
 int mgs_test_quant_dim0(const void* x, int64_t M, int64_t K, const int32_t* offsets,

@@ -153,6 +153,26 @@ int mgs_quant_groups_dim0_ws(const void *x, int64_t M, int64_t K,
                              void *stream);
 
 /*
+ * mgs_quant_groups_dim0 for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a fixed array of MGS_NOALLOC_SCRATCH_BYTES
+ * inside the library's code object, one per device, held until the process
+ * ends. Arguments, results and errors are those of mgs_quant_groups_dim0,
+ * plus MGS_ERR_UNSUPPORTED when mgs_dim0_workspace_bytes(M, K) exceeds that
+ * size (roughly M * K > 1.3e9; inputs with M <= 640 need no workspace at
+ * all). Allocates and frees nothing. The first call on a device that needs
+ * the array clears it with a kernel queued on the call's stream (a call
+ * captured before any eager one puts that clear into its graph); every call
+ * leaves it clear again. All calls on one device share the array: calls that
+ * may overlap in time (on different streams) race and give wrong results.
+ */
+#define MGS_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mgs_quant_groups_dim0_noalloc(const void *x, int64_t M, int64_t K,
+                                  const int32_t *offsets, int32_t n_groups,
+                                  uint32_t flags, void *q, float *scales,
+                                  void *stream);
+
+/*
  * Per-group scaling along dim0 with transposed outputs ([ROWWISE] Summary:
  * per-group colwise scales computed on one layout give the per-group rowwise
  * scales of its transpose; its stacked change names the transpose method as

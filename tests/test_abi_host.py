@@ -45,7 +45,8 @@ def test_status_strings(L):
 
 
 @pytest.mark.parametrize("fn", ["mgs_quant_groups_dim0", "mgs_quant_groups_dim0_ws",
-                                "mgs_quant_groups_dim0_t", "mgs_quant_groups_dim1"])
+                                "mgs_quant_groups_dim0_noalloc", "mgs_quant_groups_dim0_t",
+                                "mgs_quant_groups_dim1"])
 def test_grouped_argument_errors(L, fn):
     f = getattr(L, fn)
     ok = dict(x=A, M=64, K=128, off=A, G=4, flags=0, q=A, s=A, ws=None, wsb=0, stream=None)
@@ -82,7 +83,10 @@ def test_grouped_argument_errors(L, fn):
         assert L.mgs_dim0_workspace_bytes(2000, 128, ctypes.byref(need)) == mgs.MGS_OK
         assert need.value > 0
         assert call(M=2000, ws=A, wsb=need.value - 8) == INVALID
-    if fn.endswith("dim0") or fn.endswith("dim0_ws"):
+    if fn.endswith("_noalloc"):
+        # inputs whose workspace would exceed the fixed scratch array
+        assert call(M=200000, K=8192) == UNSUPPORTED
+    if fn.endswith("dim0") or fn.endswith("dim0_ws") or fn.endswith("_noalloc"):
         assert call(K=12) == INVALID
         assert call(s=A + 4) == INVALID
         # 1024 groups of 1024-column strips over K = 2^31 - 8: the tile bound reaches 2^31
