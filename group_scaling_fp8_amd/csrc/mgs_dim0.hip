@@ -68,12 +68,14 @@ namespace mgs {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kSlabs = kDim0Slabs;                    // vectors per thread in registers
-constexpr int kLdsSlabs = kDim0LdsSlabs;              // more per thread in LDS (dim0 only)
+constexpr int kLdsSlabs = kDim0LdsSlabs;              // vectors per thread in LDS (dim0 only)
+// vectors per thread in registers
+template <bool kT>
+constexpr int reg_slabs() { return kT ? kDim0SlabsT : kDim0Slabs; }
 // Rows of a full 128-column tile (16 lanes per row, 32 rows per slab): the
 // chunk size, and 8x / 4x / 2x the rows of the 1024 / 512 / 256-column steps.
 template <bool kT>
-constexpr int rows_w128() { return kThreads * (kSlabs + (kT ? 0 : kLdsSlabs)) / 16; }
+constexpr int rows_w128() { return kThreads * (reg_slabs<kT>() + (kT ? 0 : kLdsSlabs)) / 16; }
 static_assert(rows_w128<false>() == kDim0ChunkRows, "dim0 chunk size mismatch");
 static_assert(rows_w128<true>() == kDim0ChunkRowsT, "dim0_t chunk size mismatch");
 static_assert(kDim0ChunkRows % 8 == 0 && kDim0ChunkRowsT % 8 == 0, "strip steps");
@@ -138,6 +140,64 @@ __device__ __forceinline__ int wave_prefix_sum_dpp(int v) {
     return v;
 }
 
+// v in lane L becomes the wave-uniform value e (the lane an immediate: a
+// second scalar operand would break the one-scalar-read limit of VALU
+// instructions on this target).
+template <int L>
+__device__ __forceinline__ void write_lane(int& v, int e) {
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(e), "n"(L));
+}
+
+// Lanes L .. L + 15 of v from p[L .. L + 15] (one 64-byte scalar load).
+template <int L>
+__device__ __forceinline__ void write_lanes16(int& v, const int32_t* __restrict__ p) {
+    int e[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) e[k] = p[L + k];
+    write_lane<L + 0>(v, e[0]);   write_lane<L + 1>(v, e[1]);   write_lane<L + 2>(v, e[2]);
+    write_lane<L + 3>(v, e[3]);   write_lane<L + 4>(v, e[4]);   write_lane<L + 5>(v, e[5]);
+    write_lane<L + 6>(v, e[6]);   write_lane<L + 7>(v, e[7]);   write_lane<L + 8>(v, e[8]);
+    write_lane<L + 9>(v, e[9]);   write_lane<L + 10>(v, e[10]); write_lane<L + 11>(v, e[11]);
+    write_lane<L + 12>(v, e[12]); write_lane<L + 13>(v, e[13]); write_lane<L + 14>(v, e[14]);
+    write_lane<L + 15>(v, e[15]);
+}
+
+// Lane i's raw group end for group base + i: off[base + i] (or the equal
+// group's end), M past the last group. kScalar: the offsets come in through
+// scalar loads, 16 at a time, and are written into lanes with v_writelane.
+// A vector load queues in the CU's memory pipeline behind the tile loads of
+// the other workgroup on the CU; a scalar load takes the scalar cache
+// instead. (The transposed kernel keeps the vector load: there the scalar
+// form measured slower and needed a register spill.)
+template <bool kScalar>
+__device__ __forceinline__ int group_end_raw(const int32_t* __restrict__ off, int base, int G, int M,
+                                             int uniform_rows) {
+    const int lane = threadIdx.x & (kWave - 1);
+    if (uniform_rows >= 0) {
+        const int g = base + lane;
+        return g < G ? (g + 1) * uniform_rows : M;
+    }
+    if (!kScalar) {
+        const int g = base + lane;
+        return g < G ? off[g] : M;
+    }
+    int v = M;
+    const int n = min(G - base, kWave);
+    const int32_t* p = off + base;
+    if (n == kWave) {
+        write_lanes16<0>(v, p);
+        write_lanes16<16>(v, p);
+        write_lanes16<32>(v, p);
+        write_lanes16<48>(v, p);
+        return v;
+    }
+    for (int j = 0; j < n; ++j) {
+        const int e = p[j];
+        v = lane == j ? e : v;
+    }
+    return v;
+}
+
 // Fills t from lane src's group, tile `local` inside that group. src is
 // wave-uniform, so the fields land in scalar registers.
 __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chunk_incl, int src,
@@ -181,7 +241,7 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
 // by every wave of the workgroup; all lanes return the same tile.
 // Group ends come from off (uniform_rows < 0), or are (g + 1) * uniform_rows
 // (equal groups, e.g. the experts of a 3D weight, with no offsets array).
-template <int kRows>
+template <int kRows, bool kScalar>
 __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
                           int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -192,9 +252,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
     int carry_end = 0, carry_x = 0, carry_m = 0, carry_ch = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
-        const int raw =
-            min(max(g < G ? (uniform_rows >= 0 ? (g + 1) * uniform_rows : off[g]) : M, 0), M) &
-            -row_align;
+        const int raw = min(max(group_end_raw<kScalar>(off, base, G, M, uniform_rows), 0), M) & -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         // the previous lane's end (wave_shr:1); lane 0 keeps carry_end
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
@@ -234,9 +292,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
     carry_end = carry_m = carry_ch = 0;
     for (int base = 0; base < G; base += kWave) {
         const int g = base + lane;
-        const int raw =
-            min(max(g < G ? (uniform_rows >= 0 ? (g + 1) * uniform_rows : off[g]) : M, 0), M) &
-            -row_align;
+        const int raw = min(max(group_end_raw<kScalar>(off, base, G, M, uniform_rows), 0), M) & -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
         const GroupInfo gi = group_info<kRows>(start, end, g < G, K, team_max, lt_cap);
@@ -255,6 +311,15 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         carry_ch = __builtin_amdgcn_readlane(incl_ch, kWave - 1);
     }
     return t;
+}
+
+// The lane number, computed where it is used: the compiler cannot hoist it,
+// so addresses derived from it do not stay live (and spill) across the
+// whole kernel.
+__device__ __forceinline__ int lane_here() {
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    return lane;
 }
 
 __device__ __forceinline__ void max4(uint4& m, const uint4& t) {
@@ -276,7 +341,7 @@ __device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red)
         m.z = mag_max2(m.z, __shfl_xor(m.z, d, kWave));
         m.w = mag_max2(m.w, __shfl_xor(m.w, d, kWave));
     }
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = lane_here();
     int parts;
     if (tpr <= kWave) {
         parts = kThreads / kWave;
@@ -325,7 +390,8 @@ __device__ __forceinline__ int slab_row(int s, int rps, int ty) {
 // all exist for every lane of a full-width strip skip the per-lane checks.
 template <bool kQuad>
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t K, int r0, int nrows,
-                                          const TileGeom& q, uint4 (&v)[kSlabs]) {
+                                          const TileGeom& q, uint4 (&v)[reg_slabs<kQuad>()]) {
+    constexpr int kSlabs = reg_slabs<kQuad>();
     const int lane_row = slab_row<kQuad>(0, q.rps, q.ty);
     const int last_lane_row = slab_row<kQuad>(0, q.rps, q.rps - 1);
     const uint16_t* p = x + (int64_t)(r0 + lane_row) * K + q.col;
@@ -353,10 +419,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void load_tile_ext(const uint16_t* __restrict__ x, int64_t K, int r0,
                                               int nrows, const TileGeom& q, uint4* ext) {
     const int wave = threadIdx.x / kWave;
-    const uint16_t* p = x + (int64_t)(r0 + kSlabs * q.rps + q.ty) * K + q.col;
+    const uint16_t* p = x + (int64_t)(r0 + kDim0Slabs * q.rps + q.ty) * K + q.col;
 #pragma unroll
     for (int e = 0; e < kLdsSlabs; ++e) {
-        const int r_s = (kSlabs + e) * q.rps;
+        const int r_s = (kDim0Slabs + e) * q.rps;
         if (r_s + q.ty < nrows && q.col_ok)
             __builtin_amdgcn_global_load_lds(p, (lds_void*)(ext + e * kThreads + wave * kWave), 16, 0,
                                              kLoadNontemporal);
@@ -365,7 +431,7 @@ __device__ __forceinline__ void load_tile_ext(const uint16_t* __restrict__ x, in
 }
 
 __device__ __forceinline__ uint4 ext_slab(const uint4* ext, int e, int nrows, const TileGeom& q) {
-    if ((kSlabs + e) * q.rps + q.ty < nrows && q.col_ok) return ext[e * kThreads + threadIdx.x];
+    if ((kDim0Slabs + e) * q.rps + q.ty < nrows && q.col_ok) return ext[e * kThreads + threadIdx.x];
     return make_uint4(0u, 0u, 0u, 0u);
 }
 
@@ -488,11 +554,12 @@ __device__ __forceinline__ void dim0_body(
         long long spin_ticks, int uniform_rows, uint4* red, uint32_t* stage, uint4* ext) {
     constexpr int kRowAlign = kT ? 16 : 1;
     constexpr int kRows = rows_w128<kT>();
+    constexpr int kSlabs = reg_slabs<kT>();
     const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x) < kWave;
 
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile<kRows>(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign,
+        const Tile t = find_tile<kRows, !kT>(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign,
                                         uniform_rows, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         const TileGeom geo = tile_geom(t, K);

@@ -7,19 +7,21 @@
 
 namespace mgs {
 
-// dim0 tiling: 512-thread workgroups holding kDim0Slabs 16-byte vectors per
-// thread in registers (10240 vectors, 160 KiB of bf16), and in the plain
-// dim0 kernel kDim0LdsSlabs more per thread in LDS (4096 vectors, 64 KiB;
-// the transposed kernel's LDS holds its output stage instead). A group of
-// at most chunk_rows rows (the rows of a full 128-column tile: 896 for dim0,
-// 640 for dim0_t) is one tile per column strip. A taller group is cut into
-// chunks of at most chunk_rows rows on 128-column strips: a team of chunk
-// tiles per strip when the chunk count is at most the team limit, else a
-// column-maximum tile and a casting tile per chunk and strip.
+// dim0 tiling: 512-thread workgroups holding 16-byte vectors of the tile,
+// per thread: in the plain dim0 kernel kDim0Slabs in registers (10240
+// vectors, 160 KiB of bf16) and kDim0LdsSlabs more in LDS (4096 vectors,
+// 64 KiB); in the transposed kernel kDim0SlabsT in registers and none in
+// LDS (its LDS holds the output stage). A group of at most chunk_rows rows
+// (the rows of a full 128-column tile: 896 for dim0, 640 for dim0_t) is one
+// tile per column strip. A taller group is cut into chunks of at most
+// chunk_rows rows on 128-column strips: a team of chunk tiles per strip when
+// the chunk count is at most the team limit, else a column-maximum tile and
+// a casting tile per chunk and strip.
 constexpr int kDim0Slabs = 20;
 constexpr int kDim0LdsSlabs = 8;
-constexpr int kDim0ChunkRows = (kDim0Slabs + kDim0LdsSlabs) * 512 / 16;    // 896
-constexpr int kDim0ChunkRowsT = kDim0Slabs * 512 / 16;                     // 640
+constexpr int kDim0SlabsT = 20;
+constexpr int kDim0ChunkRows = (kDim0Slabs + kDim0LdsSlabs) * 512 / 16;   // 896
+constexpr int kDim0ChunkRowsT = kDim0SlabsT * 512 / 16;                    // 640
 // Upper limit on the chunk count of a team (the library also keeps it at
 // most the CU count, so that a team fits among the resident workgroups).
 constexpr int kDim0MaxTeam = 128;
