@@ -11,8 +11,9 @@
 // One launch, one tile per workgroup. The host sizes the grid with an upper
 // bound from (M, K, G) (it never reads the offsets); workgroups past the real
 // tile count exit as soon as they find no tile. Every wave finds its tile by
-// itself from the offsets (one vector load per 64 groups, DPP scans and a
-// ballot), so nothing stands between the launch and the tile's loads.
+// itself from the offsets (64 groups at a time: scalar loads in dim0, one
+// vector load in dim0_t; DPP scans and a ballot), so nothing stands between
+// the launch and the tile's loads.
 // Offsets are sanitised on the fly: end[g] = min(max(off[0..g]), M), clamped
 // below at 0, so any offsets array gives in-range rows.
 //
