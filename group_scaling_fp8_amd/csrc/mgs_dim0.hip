@@ -323,6 +323,13 @@ __device__ __forceinline__ int lane_here() {
     return lane;
 }
 
+// threadIdx.x through an opaque copy, for the same reason.
+__device__ __forceinline__ int tid_here() {
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    return tid;
+}
+
 __device__ __forceinline__ void max4(uint4& m, const uint4& t) {
     m.x = mag_max2(m.x, t.x);
     m.y = mag_max2(m.y, t.y);
@@ -343,16 +350,17 @@ __device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red)
         m.w = mag_max2(m.w, __shfl_xor(m.w, d, kWave));
     }
     const int lane = lane_here();
+    const int tid = tid_here();
     int parts;
     if (tpr <= kWave) {
         parts = kThreads / kWave;
-        if (lane < tpr) red[(threadIdx.x / kWave) * tpr + lane] = m;
+        if (lane < tpr) red[(tid / kWave) * tpr + lane] = m;
     } else {
         parts = kThreads / tpr;
-        red[threadIdx.x] = m;
+        red[tid] = m;
     }
     __syncthreads();
-    const int tx = threadIdx.x & (tpr - 1);
+    const int tx = tid & (tpr - 1);
     uint4 a = make_uint4(0u, 0u, 0u, 0u);
     for (int p = 0; p < parts; ++p) max4(a, red[p * tpr + tx]);
     return a;
@@ -552,17 +560,27 @@ __device__ __forceinline__ void dim0_body(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
-        long long spin_ticks, int uniform_rows, uint4* red, uint32_t* stage, uint4* ext) {
+        long long spin_ticks, int uniform_rows, int xcd_split, uint4* red, uint32_t* stage, uint4* ext) {
     constexpr int kRowAlign = kT ? 16 : 1;
     constexpr int kRows = rows_w128<kT>();
     constexpr int kSlabs = reg_slabs<kT>();
     const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x) < kWave;
 
+    // xcd_split: the dispatcher deals workgroups to the 8 XCDs in turn, and
+    // XCD x takes the tiles of columns [x K/8, (x + 1) K/8) in their usual
+    // order: the tiling of a K/8-column problem, shifted. Every strip width
+    // divides K/8 (the host checks), so each column, and each output row of
+    // the transposed kernel, is written from one XCD only.
+    const int xcol = xcd_split ? (int)(blockIdx.x & 7) : 0;
+    const int Ks = xcd_split ? K >> 3 : K;
+    const unsigned first = xcd_split ? blockIdx.x >> 3 : blockIdx.x;
+    const unsigned stride = xcd_split ? gridDim.x >> 3 : gridDim.x;
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
-    for (unsigned item = blockIdx.x; item < (unsigned)n_tiles; item += gridDim.x) {
-        const Tile t = find_tile<kRows, !kT>(off, G, M, K, team_max, lt_cap, maybe_c, kRowAlign,
-                                        uniform_rows, (int)item);
+    for (unsigned item = first; item < (unsigned)n_tiles; item += stride) {
+        Tile t = find_tile<kRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign, uniform_rows,
+                                       (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
+        t.strip += xcol * (Ks >> (t.lt + 3));
         const TileGeom geo = tile_geom(t, K);
         const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
         // a team: the tiles of one chunked group on one strip (class C: its
@@ -753,11 +771,11 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
-        long long spin_ticks, int uniform_rows) {
+        long long spin_ticks, int uniform_rows, int xcd_split) {
     __shared__ uint4 red[kThreads];
     __shared__ uint4 ext[kLdsSlabs * kThreads];     // 64 KiB: the tile's rows past the registers
     dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
-                     ws_max, spin_ticks, uniform_rows, red, nullptr, ext);
+                     ws_max, spin_ticks, uniform_rows, xcd_split, red, nullptr, ext);
 }
 
 // The same per-group scaling with transposed outputs: qT (K, M), scalesT (K, G).
@@ -765,11 +783,12 @@ __global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
-        long long spin_ticks, int uniform_rows) {
+        long long spin_ticks, int uniform_rows, int xcd_split) {
     __shared__ uint4 red[kThreads];
     __shared__ uint4 stage[kStageWords / 4];
     dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
-                    ws_max, spin_ticks, uniform_rows, red, reinterpret_cast<uint32_t*>(stage), nullptr);
+                    ws_max, spin_ticks, uniform_rows, xcd_split, red, reinterpret_cast<uint32_t*>(stage),
+                    nullptr);
 }
 
 // Zero fill of n 16-byte words (a fresh workspace; no memset node, so the
@@ -782,11 +801,14 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_
 
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
                        bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
-                       void* ws, long long spin_ticks, hipStream_t stream) {
+                       bool xcd_split, void* ws, long long spin_ticks, hipStream_t stream) {
     const int64_t chunk_rows = transposed ? kDim0ChunkRowsT : kDim0ChunkRows;
-    const int64_t n_tiles = dim0_tile_bound(M, K, G, team_max, lt_cap, chunk_rows);
+    // with xcd_split every XCD runs the tiling of K / 8 columns
+    const int64_t n_tiles = dim0_tile_bound(M, xcd_split ? K / 8 : K, G, team_max, lt_cap, chunk_rows);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
-    const int64_t grid = n_tiles < kDim0MaxGrid ? n_tiles : kDim0MaxGrid;
+    const int64_t per = n_tiles < (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid)
+                            ? n_tiles : (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid);
+    const int64_t grid = xcd_split ? 8 * per : per;
     const Dim0Workspace w = dim0_workspace(M, K);
     char* base = static_cast<char*>(ws);
     uint32_t* ws_ctr = base ? reinterpret_cast<uint32_t*>(base + w.ctr_off) : nullptr;
@@ -796,7 +818,7 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
     const int maybe_c = (int64_t)M > chunk_rows * team_max ? 1 : 0;
     hipLaunchKernelGGL(transposed ? dim0t_kernel : dim0_kernel, dim3((unsigned)grid), dim3(kThreads),
                        0, stream, x, M, K, off, G, pow2 ? 1 : 0, q, scales, (int)n_tiles, team_max,
-                       lt_cap, maybe_c, ws_ctr, ws_max, spin_ticks, uniform_rows);
+                       lt_cap, maybe_c, ws_ctr, ws_max, spin_ticks, uniform_rows, xcd_split ? 1 : 0);
     return hipGetLastError();
 }
 

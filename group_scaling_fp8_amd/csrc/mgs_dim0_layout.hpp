@@ -106,6 +106,15 @@ inline int dim0_lt_cap(int64_t M, int64_t K, int64_t G, int64_t team_max, int64_
     return lt;
 }
 
+// Whether the transposed kernel deals its tiles to the 8 XCDs by column
+// range: every strip width (at most 8 << lt_cap columns) must divide K / 8.
+// The caller then keeps teams to at most cus / 8 chunks (a quarter of the
+// workgroups one XCD holds at once), since a team's tiles all run on one
+// XCD.
+inline bool dim0_xcd_split(int64_t K, int lt_cap, int64_t cus) {
+    return cus >= 64 && cus % 8 == 0 && K > 0 && K % (int64_t(64) << lt_cap) == 0;
+}
+
 // dim0 workspace (needed only when M > kDim0ChunkRowsT), in two 256-byte
 // aligned regions: one 32-bit counter per (chunk row, 128-column strip), then
 // the column maxima of every chunk row, one 64-bit word per column pair

@@ -66,14 +66,26 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const uint16_t* __restrict
 // lane casts its 8 x 8 block and transposes it in registers; the tile goes
 // through 16 KiB of LDS so that q_t is written in whole 128-byte pieces of
 // its rows (eight lanes each), and the scales in runs of a column's blocks.
+// Tile order: each XCD (the dispatcher deals workgroups to the 8 XCDs in
+// turn) takes a contiguous run of tiles, M fastest. A tile writes 4 bytes
+// of each of its 128 scale rows; the 32 tiles that fill one 128-byte line of
+// a scale row then run on one XCD close together, so its L2 merges them and
+// writes whole lines (dealt in turn, every line was written in 4-byte
+// pieces from 8 L2s).
 constexpr int kMxTile = 128;
+constexpr int kXcds = 8;
 
 __global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                            int64_t K, int rceil,
                                                            uint8_t* __restrict__ q_t,
                                                            uint8_t* __restrict__ scales_t) {
     const int64_t nm = (M + kMxTile - 1) / kMxTile;
-    const int64_t tile_m = blockIdx.x % nm, tile_k = blockIdx.x / nm;
+    // workgroup b runs on XCD b % 8: the XCD's run of tiles starts at
+    // x * (T / 8) + min(x, T % 8)
+    const int64_t n_tiles = (int64_t)gridDim.x;
+    const int64_t xcd = blockIdx.x % kXcds, k_in = blockIdx.x / kXcds;
+    const int64_t tile = xcd * (n_tiles / kXcds) + min(xcd, n_tiles % kXcds) + k_in;
+    const int64_t tile_m = tile % nm, tile_k = tile / nm;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;        // 16 column groups, 16 row groups
     const int64_t row0 = tile_m * kMxTile + 8 * ty;                // this lane's 8 rows
     const int64_t col = tile_k * kMxTile + 8 * tx;                  // and 8 columns
@@ -115,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __res
     // index XOR-swizzled with the lane's column block, and the scale bytes as
     // [column][block]; then store whole 128-byte pieces of q_t rows
     __shared__ uint32_t st[kMxTile * kMxTile / 4];
-    __shared__ uint8_t sst[kMxTile * 4];
+    __shared__ __attribute__((aligned(4))) uint8_t sst[kMxTile * 4];
     const int w = threadIdx.x >> 6;                                 // this wave's block of the tile
     if (ok) {
         uint2 r[8];
@@ -149,28 +161,32 @@ __global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __res
         const int c = idx >> 3, p = idx & 7;
         if (c < cols && p < pieces) {
             const uint4 val = *reinterpret_cast<const uint4*>(st + c * 32 + ((4 * p) ^ (((c >> 3) & 7) << 2)));
-            *reinterpret_cast<uint4*>(q_t + (c0 + c) * M + r0 + 16 * p) = val;
+            store_stream16(q_t + (c0 + c) * M + r0 + 16 * p, val);
         }
     }
     if (threadIdx.x < cols) {
         const int c = threadIdx.x;
         const int64_t nb = M / 32;
         uint8_t* dst = scales_t + (c0 + c) * nb + r0 / 32;
-        for (int b = 0; b < (rows >> 5); ++b) dst[b] = sst[c * 4 + b];
+        if (rows == kMxTile && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+            // the column's four blocks in one 4-byte store
+            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(sst + c * 4);
+        } else {
+            for (int b = 0; b < (rows >> 5); ++b) dst[b] = sst[c * 4 + b];
+        }
     }
 }
 
 // ---- MX dequantisation ------------------------------------------------------
 // y = bf16(E4M3(q) * 2^(byte - 127)) per block of 32: the receiving side of
-// the quantise -> all-to-all -> dequantise pipeline. A lane takes 16 codes
-// (one 16-byte load, half a block, so lanes 2i and 2i + 1 share a scale
-// byte) and writes 16 bf16 values with two ordinary 16-byte stores (at the
-// MX shape: 6.3 TB/s, against 4.7 TB/s with nontemporal stores; one vector
-// per lane beats two or four). The fp8 -> fp32 conversion is exact and so is
+// the quantise -> all-to-all -> dequantise pipeline. A wave takes 1024
+// consecutive codes: lane l the 8 codes at 8l and the 8 at 512 + 8l (two
+// 8-byte loads, each wave instruction 512 contiguous bytes), and writes 16
+// bf16 values with two 16-byte nontemporal stores, each wave instruction
+// 1 KiB of whole lines of y. The fp8 -> fp32 conversion is exact and so is
 // the product with a power of two (4 significant bits, binary32 subnormals
 // kept), so the only rounding is nearest-even to bf16.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-constexpr int kDqVecs = 1;   // 16-byte code vectors per lane per workgroup
 
 // 2^(byte - 127) in binary32: normal for byte >= 1, the subnormal 2^-127 for
 // byte 0; byte 0xFF is NaN (OCP MX E8M0).
@@ -194,33 +210,31 @@ __device__ __forceinline__ uint32_t dequant2(uint32_t w, float s) {
     return bf16_rne(f.x * s) | (bf16_rne(f.y * s) << 16);
 }
 
-__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint4* __restrict__ q,
+__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint2* __restrict__ q,
                                                               const uint8_t* __restrict__ scales,
-                                                              int64_t n16, uint4* __restrict__ y) {
-    const int64_t base = (int64_t)blockIdx.x * (kThreads * kDqVecs) + threadIdx.x;
-    uint4 v[kDqVecs];
-    uint32_t sb[kDqVecs];
+                                                              int64_t n8, uint4* __restrict__ y) {
+    // units of 8 codes: this wave's 128 units start at wave_base
+    const int64_t wave_base = ((int64_t)blockIdx.x * kThreads + (threadIdx.x & ~(kWave - 1))) * 2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t u[2] = {wave_base + lane, wave_base + kWave + lane};
+    uint2 c[2];
+    uint32_t sb[2];
 #pragma unroll
-    for (int j = 0; j < kDqVecs; ++j) {
-        const int64_t vi = base + (int64_t)j * kThreads;
-        v[j] = make_uint4(0u, 0u, 0u, 0u);
-        sb[j] = 0u;
-        if (vi < n16) {
-            v[j] = load_stream(q + vi);
-            sb[j] = scales[vi >> 1];
+    for (int h = 0; h < 2; ++h) {
+        c[h] = make_uint2(0u, 0u);
+        sb[h] = 0u;
+        if (u[h] < n8) {
+            const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q + u[h]));
+            c[h] = make_uint2(t.x, t.y);
+            sb[h] = scales[u[h] >> 2];           // four units of 8 codes per block of 32
         }
     }
 #pragma unroll
-    for (int j = 0; j < kDqVecs; ++j) {
-        const int64_t vi = base + (int64_t)j * kThreads;
-        if (vi < n16) {
-            const float s = e8m0_value(sb[j]);
-            const uint4 a = make_uint4(dequant2<false>(v[j].x, s), dequant2<true>(v[j].x, s),
-                                       dequant2<false>(v[j].y, s), dequant2<true>(v[j].y, s));
-            const uint4 b = make_uint4(dequant2<false>(v[j].z, s), dequant2<true>(v[j].z, s),
-                                       dequant2<false>(v[j].w, s), dequant2<true>(v[j].w, s));
-            y[2 * vi] = a;
-            y[2 * vi + 1] = b;
+    for (int h = 0; h < 2; ++h) {
+        if (u[h] < n8) {
+            const float s = e8m0_value(sb[h]);
+            store_stream16(y + u[h], make_uint4(dequant2<false>(c[h].x, s), dequant2<true>(c[h].x, s),
+                                                dequant2<false>(c[h].y, s), dequant2<true>(c[h].y, s)));
         }
     }
 }
@@ -276,11 +290,11 @@ hipError_t launch_mx_dim1(const uint16_t* x, int64_t M, int64_t K, bool rceil, u
 
 hipError_t launch_mx_dequant(const uint8_t* q, const uint8_t* scales, int64_t n_elems, uint16_t* y,
                              hipStream_t stream) {
-    const int64_t n16 = n_elems / 16;
-    const int64_t per_block = (int64_t)kThreads * kDqVecs;
-    const int64_t blocks = (n16 + per_block - 1) / per_block;
+    const int64_t n8 = n_elems / 8;
+    const int64_t per_block = (int64_t)kThreads * 2;
+    const int64_t blocks = (n8 + per_block - 1) / per_block;
     hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(q), scales, n16, reinterpret_cast<uint4*>(y));
+                       reinterpret_cast<const uint2*>(q), scales, n8, reinterpret_cast<uint4*>(y));
     return hipGetLastError();
 }
 

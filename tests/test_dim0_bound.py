@@ -166,3 +166,23 @@ def test_chunk_bound_covers_every_chunked_split(bound_tool, C):
             rows = M // n
             worst = max(worst, n * math.ceil(rows / C))
         assert chunks >= worst, (M, C, chunks, worst)
+
+
+@pytest.mark.parametrize("K,max_lt", [(8192, 7), (16384, 7), (4096, 6), (512, 3), (1024, 4)])
+def test_xcd_split_tiles_are_eight_copies(bound_tool, K, max_lt):
+    """When the transposed kernel deals tiles to the 8 XCDs by column range
+    (K / 8 a multiple of the widest strip), every group's tiles are 8 copies
+    of the tiles of a K / 8-column problem, so 8 x the bound for K / 8 covers
+    the launch."""
+    assert K % (64 << max_lt) == 0
+    C = 640
+    for team_max in (1, 32):
+        Rs = [0, 1, 16, 80, 81, 161, 321, 640, 641, 1281, 5121, 20481]
+        got = bound_tool([(R, K, 1, team_max, max_lt, C) for R in Rs])
+        part = bound_tool([(R, K // 8, 1, team_max, max_lt, C) for R in Rs])
+        for R, (_, _, full), (_, _, eighth) in zip(Rs, got, part):
+            assert full == 8 * eighth, (R, K, max_lt, team_max, full, eighth)
+        for M, G in ((16640, 64), (3200, 3), (20480, 1)):
+            (b8, _, _), = bound_tool([(M, K // 8, G, team_max, max_lt, C)])
+            exact = int(worst_splits(M, K, G, team_max, max_lt, C)[G][M])
+            assert 8 * b8 >= exact, (M, K, G, team_max, b8, exact)

@@ -112,3 +112,29 @@ def test_dim0_t_unaligned_offsets_stay_in_bounds():
     x = data(7, 320, 136)
     for off in ([100, 37, 320], [5, 320], [-3, 400, 320], [320]):
         run_dim0_t(x, np.array(off, np.int32))
+
+
+# K a multiple of 8 times the widest strip: the tiles are dealt to the XCDs
+# by column range (each XCD the tiling of K / 8 columns), teams included
+@pytest.mark.parametrize("team_max", [None, 1])
+@pytest.mark.parametrize("K,sizes", [
+    (8192, [0, 1600, 48, 1552, 16]),          # 3-chunk teams, an empty group, short groups
+    (16384, [96, 704, 0, 320]),               # 2-chunk team, 1024- to 128-column strips
+    (8192, [2048]),                           # one group, one 4-chunk team per strip
+])
+def test_dim0_t_tiles_by_column_range(K, sizes, team_max):
+    off = np.cumsum(sizes).astype(np.int32)
+    M = int(off[-1])
+    x = data(M + K, M, K)
+    if team_max is None:
+        check(x, off, "column ranges %s K=%d" % (sizes, K))
+        return
+    gq, gs = Guarded((K, M), torch.uint8), Guarded((K, len(off)), torch.float32)
+    mgs.api._test_quant_dim0(to_dev(x), to_dev(off), gq.view, gs.view, transposed=True,
+                             team_max=team_max, workspace=mgs.dim0_workspace(M, K))
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    rq, rs = oracle.quant_groups_dim0_t(x, off)
+    assert_same_bytes(gs.numpy(), rs, "column ranges, team limit 1, scales_t")
+    assert_same_bytes(gq.numpy(), rq, "column ranges, team limit 1, q_t")
