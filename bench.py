@@ -233,8 +233,13 @@ def main():
            and np.array_equal(s1[rows].cpu().numpy().view(np.uint32), rs1.view(np.uint32)))
 
     kernels = None
+    inputs = {"numpy": np.__version__,
+              "generator": "numpy default_rng (PCG64), seeds in group_scaling_fp8_amd/workloads.py",
+              "sha256": {"T (16640,8192) bf16, seed 4": hashlib.sha256(T.tobytes()).hexdigest(),
+                         "offsets G=64, seed 104": hashlib.sha256(off.tobytes()).hexdigest()}}
     if not args.no_kernels:
-        kernels = per_config_table(torch, mgs, wl, dev, T, Tt)
+        kernels = per_config_table(torch, mgs, wl, dev, T, Tt, inputs["sha256"])
+        kernels += host_call_cost(torch, mgs, wl, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -262,6 +267,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "inputs": inputs,
     }
     print(json.dumps(out), flush=True)
 
@@ -271,7 +277,7 @@ def main():
 # specific names come first
 KERNELS = (("copy_kernel", "copy"), ("mx_dim1_kernel", "mx_dim1_kernel"),
            ("mx_dequant_kernel", "mx_dequant_kernel"), ("mx_kernel", "mx_kernel"),
-           ("dim0_epoch_bump_kernel", "dim0_epoch_bump_kernel"), ("dim0t_kernel", "dim0t_kernel"),
+           ("zero_kernel", "zero_kernel"), ("dim0t_kernel", "dim0t_kernel"),
            ("dim0_kernel", "dim0_kernel"), ("dim1_kernel", "dim1_kernel"))
 COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
 
@@ -407,7 +413,9 @@ def steady_us(torch, fn, reps=20):
     return a.elapsed_ms(b) * 1e3 / reps
 
 
-def per_config_table(torch, mgs, wl, dev, T, Tt):
+def per_config_table(torch, mgs, wl, dev, T, Tt, sha):
+    """Per-config kernel times; records each generated input's sha256 in
+    `sha` (config name -> digest of x's bytes, then the offsets')."""
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
     rows = []
 
@@ -430,6 +438,7 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
             % (name, med, rows[-1]["algorithmic_GBps"], sty, rows[-1]["steady_GBps"]))
 
     def grouped(w):
+        sha[w.name] = w.sha256()
         x = torch.from_numpy(w.x.view(np.int16)).to(dev)
         o = torch.from_numpy(w.offsets).to(dev)
         f = mgs.mgs_quant_groups_dim0 if w.kind == "dim0" else mgs.mgs_quant_groups_dim1
@@ -469,6 +478,7 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
         lambda: (lambda: mgs.mgs_quant_experts_dim1(w3, q=q3, scales=s3)))
     del w3, q3, s3
     c5 = wl.c5_mx()
+    sha[c5.name + ", seed 5"] = c5.sha256()
     x5 = torch.from_numpy(c5.x.view(np.int16)).to(dev)
     for mode, nm in ((mgs.MGS_MX_FLOOR, "FLOOR"), (mgs.MGS_MX_RCEIL, "RCEIL")):
         q, s = mgs.mgs_mx_quant_dim0(x5, mode)
@@ -505,6 +515,56 @@ def per_config_table(torch, mgs, wl, dev, T, Tt):
         2 * src.numel(), lambda: (lambda: mgs.mgs_copy(src, dst)))
     del x5, src, dst, flush
     torch.cuda.empty_cache()
+    return rows
+
+
+def host_call_cost(torch, mgs, wl, dev, n=2000):
+    """Host time per call of the C ABI alone: a ctypes loop over
+    mgs_quant_groups_dim0 (the library's own workspace) and
+    mgs_quant_groups_dim1 on the (256, 4096) G=4 configuration, with device
+    pointers and the stream handle prepared once (no torch in the loop), and
+    the same launches through the Python binding. The kernels queue up
+    behind the host; the device is synchronised only around each loop."""
+    import ctypes
+    w = wl.c1_dim0_small()
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    o = torch.from_numpy(w.offsets).to(dev)
+    M, K = w.x.shape
+    G = len(w.offsets)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s0 = torch.empty((G, K), dtype=torch.float32, device=dev)
+    s1 = torch.empty((M, G), dtype=torch.float32, device=dev)
+    o1 = torch.from_numpy(wl.uniform_group_offsets(np.random.default_rng(9), K, G)).to(dev)
+    L = mgs.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xp, op, o1p, qp = x.data_ptr(), o.data_ptr(), o1.data_ptr(), q.data_ptr()
+    s0p, s1p = s0.data_ptr(), s1.data_ptr()
+    rows = []
+
+    def timed(name, fn):
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        us = (t1 - t0) * 1e6 / n
+        rows.append({"config": name, "kind": "host_call", "us_host_per_call": round(us, 2),
+                     "us_per_call_with_drain": round((t2 - t0) * 1e6 / n, 2)})
+        log("  %-52s %6.2f us host per call (%6.2f with the queue drained)"
+            % (name, us, (t2 - t0) * 1e6 / n))
+
+    log("host cost per call, (256, 4096) G=4:")
+    f0, f1 = L.mgs_quant_groups_dim0, L.mgs_quant_groups_dim1
+    timed("C ABI via ctypes: mgs_quant_groups_dim0",
+          lambda: f0(xp, M, K, op, G, 0, qp, s0p, stream))
+    timed("C ABI via ctypes: mgs_quant_groups_dim1",
+          lambda: f1(xp, M, K, o1p, G, 0, qp, s1p, stream))
+    timed("Python binding: mgs_quant_groups_dim0",
+          lambda: mgs.mgs_quant_groups_dim0(x, o, q=q, scales=s0))
     return rows
 
 

@@ -17,8 +17,18 @@ from ._lib import MGS_FLAG_POW2_SCALE, MGS_FLAG_VALIDATE, MGS_MX_FLOOR, MGS_MX_R
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
 
-def _stream_handle(stream) -> int:
+try:
+    _raw_stream = torch._C._cuda_getCurrentRawStream     # the current stream of a device, as an int
+except AttributeError:  # pragma: no cover - other torch builds
+    _raw_stream = None
+
+
+def _stream_handle(stream, t: Optional[torch.Tensor] = None) -> int:
+    """The hipStream_t to launch on: `stream` if given, else torch's current
+    stream on t's device."""
     if stream is None:
+        if _raw_stream is not None and t is not None:
+            return _raw_stream(t.get_device())
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -26,7 +36,7 @@ def _stream_handle(stream) -> int:
 def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
     if t.dtype not in dtypes:
         raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
@@ -36,12 +46,17 @@ def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None):
         raise ValueError("%s must be contiguous" % name)
 
 
+_U8_LIKE = (torch.uint8, torch.float8_e4m3fn)
+
+
 def _out(t, shape, dtype, device, name):
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device)
-    _need(t, name, (dtype,) if dtype != torch.uint8 else (torch.uint8, torch.float8_e4m3fn))
-    if tuple(t.shape) != tuple(shape):
+    _need(t, name, (dtype,) if dtype != torch.uint8 else _U8_LIKE)
+    if t.shape != shape:
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.get_device() != device.index:
+        raise ValueError("%s is on %s, the input on %s" % (name, t.device, device))
     return t
 
 
@@ -92,13 +107,13 @@ def mgs_quant_groups_dim0(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = F
     if workspace is None:
         st = lib().mgs_quant_groups_dim0(x.data_ptr(), M, K, offsets.data_ptr(), G,
                                          _flags(pow2, validate), q.data_ptr(),
-                                         scales.data_ptr(), _stream_handle(stream))
+                                         scales.data_ptr(), _stream_handle(stream, x))
         check("mgs_quant_groups_dim0", st)
     else:
         wp, wb = _ws_args(workspace)
         st = lib().mgs_quant_groups_dim0_ws(x.data_ptr(), M, K, offsets.data_ptr(), G,
                                             _flags(pow2, validate), q.data_ptr(),
-                                            scales.data_ptr(), wp, wb, _stream_handle(stream))
+                                            scales.data_ptr(), wp, wb, _stream_handle(stream, x))
         check("mgs_quant_groups_dim0_ws", st)
     return q, scales
 
@@ -118,7 +133,7 @@ def mgs_quant_groups_dim0_noalloc(x: torch.Tensor, offsets: torch.Tensor, pow2: 
     scales = _out(scales, (G, K), torch.float32, x.device, "scales")
     st = lib().mgs_quant_groups_dim0_noalloc(x.data_ptr(), M, K, offsets.data_ptr(), G,
                                              _flags(pow2, validate), q.data_ptr(),
-                                             scales.data_ptr(), _stream_handle(stream))
+                                             scales.data_ptr(), _stream_handle(stream, x))
     check("mgs_quant_groups_dim0_noalloc", st)
     return q, scales
 
@@ -140,7 +155,7 @@ def mgs_quant_groups_dim0_t(x: torch.Tensor, offsets: torch.Tensor, pow2: bool =
     wp, wb = _ws_args(workspace)
     st = lib().mgs_quant_groups_dim0_t(x.data_ptr(), M, K, offsets.data_ptr(), G,
                                        _flags(pow2, validate), q_t.data_ptr(),
-                                       scales_t.data_ptr(), wp, wb, _stream_handle(stream))
+                                       scales_t.data_ptr(), wp, wb, _stream_handle(stream, x))
     check("mgs_quant_groups_dim0_t", st)
     return q_t, scales_t
 
@@ -156,7 +171,7 @@ def mgs_quant_experts_dim1(w: torch.Tensor, pow2: bool = False, q: Optional[torc
     scales = _out(scales, (E, D2), torch.float32, w.device, "scales")
     wp, wb = _ws_args(workspace)
     st = lib().mgs_quant_experts_dim1(w.data_ptr(), E, D1, D2, MGS_FLAG_POW2_SCALE if pow2 else 0,
-                                      q.data_ptr(), scales.data_ptr(), wp, wb, _stream_handle(stream))
+                                      q.data_ptr(), scales.data_ptr(), wp, wb, _stream_handle(stream, w))
     check("mgs_quant_experts_dim1", st)
     return q, scales
 
@@ -174,7 +189,7 @@ def mgs_quant_groups_dim1(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = F
     scales = _out(scales, (M, G), torch.float32, x.device, "scales")
     st = lib().mgs_quant_groups_dim1(x.data_ptr(), M, K, offsets.data_ptr(), G,
                                      _flags(pow2, validate), q.data_ptr(),
-                                     scales.data_ptr(), _stream_handle(stream))
+                                     scales.data_ptr(), _stream_handle(stream, x))
     check("mgs_quant_groups_dim1", st)
     return q, scales
 
@@ -197,7 +212,7 @@ def mgs_mx_quant_dim0(x: torch.Tensor, mode: int = MGS_MX_FLOOR,
         _need(offsets, "offsets", (torch.int32,), 1)
         off_ptr, G = offsets.data_ptr(), offsets.shape[0]
     st = lib().mgs_mx_quant_dim0(x.data_ptr(), M, K, off_ptr, G, int(mode), q.data_ptr(),
-                                 scales.data_ptr(), _stream_handle(stream))
+                                 scales.data_ptr(), _stream_handle(stream, x))
     check("mgs_mx_quant_dim0", st)
     return q, scales
 
@@ -213,7 +228,7 @@ def mgs_mx_quant_dim1(x: torch.Tensor, mode: int = MGS_MX_FLOOR, q_t: Optional[t
     q_t = _out(q_t, (K, M), torch.uint8, x.device, "q_t")
     scales_t = _out(scales_t, (K, M // 32), torch.uint8, x.device, "scales_t")
     st = lib().mgs_mx_quant_dim1(x.data_ptr(), M, K, int(mode), q_t.data_ptr(), scales_t.data_ptr(),
-                                 _stream_handle(stream))
+                                 _stream_handle(stream, x))
     check("mgs_mx_quant_dim1", st)
     return q_t, scales_t
 
@@ -235,7 +250,7 @@ def mgs_mx_dequant_dim0(q: torch.Tensor, scales: torch.Tensor, y: Optional[torch
         if tuple(y.shape) != (M, K):
             raise ValueError("y has shape %s, expected %s" % (tuple(y.shape), (M, K)))
     st = lib().mgs_mx_dequant_dim0(q.data_ptr(), scales.data_ptr(), M, K, y.data_ptr(),
-                                   _stream_handle(stream))
+                                   _stream_handle(stream, q))
     check("mgs_mx_dequant_dim0", st)
     return y
 
@@ -245,7 +260,7 @@ def mgs_cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,
     """E4M3 cast of a float32 tensor (numel % 4 == 0) with the library's cast."""
     _need(x, "x", (torch.float32,))
     out = _out(out, tuple(x.shape), torch.uint8, x.device, "out")
-    st = lib().mgs_cast_e4m3(x.data_ptr(), x.numel(), out.data_ptr(), _stream_handle(stream))
+    st = lib().mgs_cast_e4m3(x.data_ptr(), x.numel(), out.data_ptr(), _stream_handle(stream, x))
     check("mgs_cast_e4m3", st)
     return out
 
@@ -257,7 +272,7 @@ def mgs_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("mgs_copy needs contiguous tensors of equal byte size")
-    st = lib().mgs_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream))
+    st = lib().mgs_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream, src))
     check("mgs_copy", st)
     return dst
 
@@ -286,5 +301,5 @@ def _test_quant_dim0(x: torch.Tensor, offsets: Optional[torch.Tensor], q: torch.
     st = lib().mgs_test_quant_dim0(x.data_ptr(), M, K, off_ptr, G, int(uniform_rows),
                                    MGS_FLAG_POW2_SCALE if pow2 else 0, 1 if transposed else 0,
                                    q.data_ptr(), scales.data_ptr(), wp, wb, int(spin_ticks),
-                                   int(team_max), _stream_handle(stream))
+                                   int(team_max), _stream_handle(stream, x))
     check("mgs_test_quant_dim0", st)
