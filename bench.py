@@ -117,8 +117,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-config table")
     ap.add_argument("--counter-run", type=int, default=0, metavar="REPS",
-                    help="only launch each hot kernel (and a 256 MiB calibration copy) REPS times, "
-                         "for rocprofv3 counter collection")
+                    help="only launch each case of counter_cases() (a 256 MiB calibration copy, "
+                         "then the library's kernels) REPS times, for rocprofv3 counter collection; "
+                         "with --rocprof-summary, the REPS those runs used")
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="print a markdown summary of rocprofv3 output under DIR (trace/, fetch/, "
                          "write/ from the commands in profiles/README.md) and write "
@@ -128,11 +129,11 @@ def main():
     args = ap.parse_args()
 
     if args.rocprof_summary:
-        rocprof_summary(args.rocprof_summary)
+        rocprof_summary(args.rocprof_summary, args.counter_run or 3)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the per-group cast needs no cross-GPU exchange, and "
-              "multi-GPU runs are not part of this build (got --gpus %d)" % args.gpus,
+              "this benchmark runs on one GPU only (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
@@ -263,7 +264,8 @@ def main():
                    "M": M, "K": K, "groups": G, "in": "bf16", "out": "e4m3 + fp32 scales",
                    "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
                    "parity_spot_check": bool(ok0 and ok1),
-                   "device": torch.cuda.get_device_name(0)},
+                   "device": torch.cuda.get_device_name(0)
+                   or torch.cuda.get_device_properties(0).gcnArchName},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
@@ -302,85 +304,150 @@ def _stats_table(path):
     return out
 
 
-def rocprof_summary(d):
+def counter_cases():
+    """The counter run's launches in order: (label, kernel, algorithmic bytes
+    per launch). Bytes: bf16 read once, E4M3 written once, fp32 scales
+    written and int32 offsets read (grouped casts); E8M0 scales (MX);
+    for the dequantisation the E4M3 codes and scales read and bf16 written."""
+    def dim0(M, K, G):
+        return 3 * M * K + 4 * G * K + 4 * G
+
+    def dim1(M, K, G):
+        return 3 * M * K + 4 * M * G + 4 * G
+
+    mx = 3 * 131072 * 5120 + 131072 * 5120 // 32
+    return [("copy 256 MiB (calibration)", "copy", 2 * COPY_BYTES),
+            ("dim0 (16640,8192) G=64", "dim0_kernel", dim0(16640, 8192, 64)),
+            ("dim0 (16640,8192) G=1", "dim0_kernel", dim0(16640, 8192, 1)),
+            ("dim0 (256,4096) G=4", "dim0_kernel", dim0(256, 4096, 4)),
+            ("dim0 (4096,4096) G=16 pow2", "dim0_kernel", dim0(4096, 4096, 16)),
+            ("dim0 (65536,4096) G=8", "dim0_kernel", dim0(65536, 4096, 8)),
+            ("dim1 (8192,16640) G=64", "dim1_kernel", dim1(8192, 16640, 64)),
+            ("dim1 (8192,16640) G=16", "dim1_kernel", dim1(8192, 16640, 16)),
+            ("dim1 (8192,16640) G=1", "dim1_kernel", dim1(8192, 16640, 1)),
+            ("mx dim0 (131072,5120) FLOOR", "mx_kernel", mx),
+            ("mx dim0 (131072,5120) RCEIL", "mx_kernel", mx),
+            ("dim0_t (16640,8192) G=64", "dim0t_kernel", dim0(16640, 8192, 64)),
+            ("mx dim1 (131072,5120) FLOOR", "mx_dim1_kernel", mx),
+            ("mx dequant (131072,5120)", "mx_dequant_kernel", mx)]
+
+
+def _dispatches(path, name_col, reps, extra):
+    """Rows of a rocprofv3 CSV for the counter run's measured launches, in
+    dispatch order, grouped per case: the last len(cases) * reps rows whose
+    kernel is one of the library's."""
     import csv
+    rows = [r for r in csv.DictReader(open(path)) if _short(r[name_col])]
+    for key in ("Dispatch_Id", "Start_Timestamp"):
+        if rows and key in rows[0]:
+            rows.sort(key=lambda r: int(r[key]))
+            break
+    cases = counter_cases()
+    rows = rows[-len(cases) * reps:]
+    if len(rows) != len(cases) * reps:
+        raise SystemExit("%s: %d dispatches, expected %d" % (path, len(rows), len(cases) * reps))
+    out = []
+    for i, (label, kernel, _) in enumerate(cases):
+        mine = rows[i * reps:(i + 1) * reps]
+        for r in mine:
+            if _short(r[name_col]) != kernel:
+                raise SystemExit("%s: case %r ran %s" % (path, label, r[name_col][:60]))
+        out.append([extra(r) for r in mine])
+    return out
+
+
+def rocprof_summary(d, reps):
+    """Markdown summary of a counter run (kernel trace, FETCH_SIZE and
+    WRITE_SIZE passes under d/trace, d/fetch, d/write), one row per case;
+    also writes profiles/hbm_traffic.json."""
     bench_stats = os.path.join(d, "bench", "run_kernel_stats.csv")
     if os.path.exists(bench_stats):
         print("\n".join(["## benchmark command (steps after warmup, with and without events)", ""]
                         + _stats_table(bench_stats) + [""]))
-    out = ["## counter run (one launch at a time after a cache sweep)", ""]
-    out += _stats_table(os.path.join(d, "trace", "run_kernel_stats.csv"))
+    cases = counter_cases()
+    dur = _dispatches(os.path.join(d, "trace", "run_kernel_trace.csv"), "Kernel_Name", reps,
+                      lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     kib = {}
     for counter in ("fetch", "write"):
-        path = os.path.join(d, counter, "run_counter_collection.csv")
-        if not os.path.exists(path):
-            continue
-        per = {}
-        for r in csv.DictReader(open(path)):
-            k = _short(r["Kernel_Name"])
-            if k:
-                per.setdefault(k, []).append(float(r["Counter_Value"]))
-        kib[counter] = {k: sum(v) / len(v) for k, v in per.items()}
-    traffic = None
-    if "fetch" in kib and "write" in kib and "copy" in kib["fetch"]:
-        ff = COPY_BYTES / 1024.0 / kib["fetch"]["copy"]
-        wf = COPY_BYTES / 1024.0 / kib["write"]["copy"]
-        out += ["", "FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f (the copy kernel moves %d B each way)"
-                % (ff, wf, COPY_BYTES), "",
-                "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per launch |",
-                "|---|---|---|---|"]
-        traffic = {"source_hash": kernel_source_hash(), "fetch_scale": ff, "write_scale": wf,
-                   "kernels": {}}
-        for k in sorted(kib["fetch"]):
-            if k == "copy" or k not in kib["write"]:
-                continue
-            b = kib["fetch"][k] * 1024 * ff + kib["write"][k] * 1024 * wf
-            traffic["kernels"][k] = {"fetch_kib": kib["fetch"][k], "write_kib": kib["write"][k],
-                                     "bytes_per_launch": round(b)}
-            out.append("| %s | %.1f | %.1f | %d |" % (k, kib["fetch"][k], kib["write"][k], b))
-        with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
-            json.dump(traffic, f, indent=1)
+        kib[counter] = _dispatches(os.path.join(d, counter, "run_counter_collection.csv"),
+                                   "Kernel_Name", reps, lambda r: float(r["Counter_Value"]))
+    mean = lambda v: sum(v) / len(v)
+    ff = COPY_BYTES / 1024.0 / mean(kib["fetch"][0])
+    wf = COPY_BYTES / 1024.0 / mean(kib["write"][0])
+    out = ["## counter run (one launch at a time after a 1 GiB read sweep; %d launches per case)" % reps,
+           "", "FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f (the copy kernel reads and writes %d B)"
+           % (ff, wf, COPY_BYTES), "",
+           "| case | kernel | avg us | algorithmic MB | HBM read MB | HBM written MB | HBM / algorithmic "
+           "| algorithmic GB/s |", "|---|---|---|---|---|---|---|---|"]
+    traffic = {"source_hash": kernel_source_hash(), "fetch_scale": ff, "write_scale": wf,
+               "cases": {}, "kernels": {}}
+    for i, (label, kernel, alg) in enumerate(cases):
+        us = mean(dur[i])
+        rd = mean(kib["fetch"][i]) * 1024 * ff
+        wr = mean(kib["write"][i]) * 1024 * wf
+        traffic["cases"][label] = {"kernel": kernel, "avg_us": round(us, 2), "algorithmic_bytes": alg,
+                                   "fetch_kib": mean(kib["fetch"][i]), "write_kib": mean(kib["write"][i]),
+                                   "bytes_per_launch": round(rd + wr)}
+        # the first case of each kernel is the one its roofline is quoted on
+        traffic["kernels"].setdefault(kernel, traffic["cases"][label])
+        out.append("| %s | %s | %.2f | %.1f | %.1f | %.1f | %.3f | %.0f |" % (
+            label, kernel, us, alg / 1e6, rd / 1e6, wr / 1e6, (rd + wr) / alg, alg / us / 1e3))
+    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
     print("\n".join(out))
 
 
 def counter_run(torch, mgs, wl, dev, reps):
-    """Launches each hot kernel `reps` times with nothing else on the GPU but
-    the cache-evicting read between launches, so a counter collector sees
-    one dispatch per launch: the 256 MiB copy kernel (known traffic,
-    268435456 B read + written), dim0 on T (16640, 8192) G=64, dim1 on T^T
-    G=64, the MX cast on (131072, 5120) FLOOR and RCEIL, the transposed dim0
-    on T G=64, the MX dim1 cast and the MX dequantisation at the MX shape."""
+    """Launches each case of counter_cases() `reps` times, in that order,
+    with nothing else on the GPU but a cache-evicting read before each
+    launch, so a counter collector sees one dispatch per launch. Every
+    output buffer and workspace is made first, by calls outside the
+    measured loops."""
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     T = wl.token_major_gradient()
-    off = torch.from_numpy(wl.target_offsets(64)).to(dev)
+    g64 = torch.from_numpy(wl.target_offsets(64)).to(dev)
+    g16 = torch.from_numpy(wl.target_offsets(16)).to(dev)
+    g1 = torch.from_numpy(np.array([T.shape[0]], np.int32)).to(dev)
     x0 = torch.from_numpy(T.view(np.int16)).to(dev)
     x1 = torch.from_numpy(np.ascontiguousarray(T.T).view(np.int16)).to(dev)
     del T
+    small = []
+    for w in (wl.c1_dim0_small(), wl.c2_dim0_pow2(), wl.c3_dim0_large()):
+        small.append((torch.from_numpy(w.x.view(np.int16)).to(dev), torch.from_numpy(w.offsets).to(dev),
+                      w.pow2))
     c5 = wl.c5_mx()
     x5 = torch.from_numpy(c5.x.view(np.int16)).to(dev)
     del c5
-    q0, s0 = mgs.mgs_quant_groups_dim0(x0, off)
-    q1, s1 = mgs.mgs_quant_groups_dim1(x1, off)
+
+    def grouped(f, x, o, pow2=False):
+        q, s = f(x, o, pow2)
+        return lambda: f(x, o, pow2, q=q, scales=s)
+
+    dim0, dim1 = mgs.mgs_quant_groups_dim0, mgs.mgs_quant_groups_dim1
     q5, s5 = mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR)
-    qt, st = mgs.mgs_quant_groups_dim0_t(x0, off)
+    qt, st = mgs.mgs_quant_groups_dim0_t(x0, g64)
     qd1, sd1 = mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR)
     yd = mgs.mgs_mx_dequant_dim0(q5, s5)
     runs = [lambda: mgs.mgs_copy(src, dst),
-            lambda: mgs.mgs_quant_groups_dim0(x0, off, q=q0, scales=s0),
-            lambda: mgs.mgs_quant_groups_dim1(x1, off, q=q1, scales=s1),
-            lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR, q=q5, scales=s5),
-            lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q5, scales=s5),
-            lambda: mgs.mgs_quant_groups_dim0_t(x0, off, q_t=qt, scales_t=st),
-            lambda: mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR, q_t=qd1, scales_t=sd1),
-            lambda: mgs.mgs_mx_dequant_dim0(q5, s5, y=yd)]
-    for fn in runs:
+            grouped(dim0, x0, g64), grouped(dim0, x0, g1)] + \
+        [grouped(dim0, x, o, p) for x, o, p in small] + \
+        [grouped(dim1, x1, g64), grouped(dim1, x1, g16), grouped(dim1, x1, g1),
+         lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR, q=q5, scales=s5),
+         lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q5, scales=s5),
+         lambda: mgs.mgs_quant_groups_dim0_t(x0, g64, q_t=qt, scales_t=st),
+         lambda: mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR, q_t=qd1, scales_t=sd1),
+         lambda: mgs.mgs_mx_dequant_dim0(q5, s5, y=yd)]
+    assert len(runs) == len(counter_cases())
+    torch.cuda.synchronize()
+    for (label, _, _), fn in zip(counter_cases(), runs):
         for _ in range(reps):
             flush.max()
             fn()
             torch.cuda.synchronize()
-    log("counter run done: %d launches of each kernel" % reps)
+        log("counter run: %s x%d" % (label, reps))
+    log("counter run done: %d launches of each case" % reps)
 
 
 def timed_us(torch, fn, flush, reps=20):
