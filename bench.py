@@ -466,12 +466,18 @@ def timed_us(torch, fn, flush, reps=20):
     return float(np.median(ts)), float(np.min(ts))
 
 
-def steady_us(torch, fn, reps=20):
+def steady_us(torch, fn, reps=20, lead=3):
     """Average of `reps` back-to-back launches with no flush between them:
-    each launch also pays for writing back what the one before left dirty."""
+    each launch also pays for writing back what the one before left dirty.
+    `lead` launches are queued before the first event, so the timed block
+    starts on a busy stream: it measures the GPU's time per launch, not the
+    submission latency of the first one (the host's cost per call is
+    measured on its own in host_call_cost)."""
     st = torch.cuda.current_stream()
     torch.cuda.synchronize()
     a, b = HipEvent(), HipEvent()
+    for _ in range(lead):
+        fn()
     a.record(st)
     for _ in range(reps):
         fn()
