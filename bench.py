@@ -234,17 +234,18 @@ def main():
            and np.array_equal(s1[rows].cpu().numpy().view(np.uint32), rs1.view(np.uint32)))
 
     kernels = None
+    samples = {}
     inputs = {"numpy": np.__version__,
               "generator": "numpy default_rng (PCG64), seeds in group_scaling_fp8_amd/workloads.py",
               "sha256": {"T (16640,8192) bf16, seed 4": hashlib.sha256(T.tobytes()).hexdigest(),
                          "offsets G=64, seed 104": hashlib.sha256(off.tobytes()).hexdigest()}}
     if not args.no_kernels:
-        kernels = per_config_table(torch, mgs, wl, dev, T, Tt, inputs["sha256"])
+        kernels = per_config_table(torch, mgs, wl, dev, T, Tt, inputs["sha256"], samples)
         kernels += host_call_cost(torch, mgs, wl, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(T, Tt, off, args.cpu_cols)
+        cpu = cpu_baseline(T, Tt, off, args.cpu_cols, samples)
 
     out = {
         "metric": "achieved HBM GB/s (% of peak) per-group fp8 scale+cast, (16640,8192) bf16 G=64",
@@ -304,6 +305,13 @@ def _stats_table(path):
     return out
 
 
+def experts_weight(torch, dev):
+    """The (16, 5120, 8192) bf16 expert weight, randn * 0.02, drawn on the
+    GPU from torch's generator with seed 7."""
+    gen = torch.Generator(device=dev).manual_seed(7)
+    return (torch.randn((16, 5120, 8192), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+
+
 def counter_cases():
     """The counter run's launches in order: (label, kernel, algorithmic bytes
     per launch). Bytes: bf16 read once, E4M3 written once, fp32 scales
@@ -319,17 +327,19 @@ def counter_cases():
     return [("copy 256 MiB (calibration)", "copy", 2 * COPY_BYTES),
             ("dim0 (16640,8192) G=64", "dim0_kernel", dim0(16640, 8192, 64)),
             ("dim0 (16640,8192) G=1", "dim0_kernel", dim0(16640, 8192, 1)),
+            ("dim0 (16640,8192) G=8 even", "dim0_kernel", dim0(16640, 8192, 8)),
             ("dim0 (256,4096) G=4", "dim0_kernel", dim0(256, 4096, 4)),
             ("dim0 (4096,4096) G=16 pow2", "dim0_kernel", dim0(4096, 4096, 16)),
-            ("dim0 (65536,4096) G=8", "dim0_kernel", dim0(65536, 4096, 8)),
+            ("dim0 (65536,4096) G=8 dirichlet", "dim0_kernel", dim0(65536, 4096, 8)),
             ("dim1 (8192,16640) G=64", "dim1_kernel", dim1(8192, 16640, 64)),
             ("dim1 (8192,16640) G=16", "dim1_kernel", dim1(8192, 16640, 16)),
             ("dim1 (8192,16640) G=1", "dim1_kernel", dim1(8192, 16640, 1)),
             ("mx dim0 (131072,5120) FLOOR", "mx_kernel", mx),
             ("mx dim0 (131072,5120) RCEIL", "mx_kernel", mx),
-            ("dim0_t (16640,8192) G=64", "dim0t_kernel", dim0(16640, 8192, 64)),
-            ("mx dim1 (131072,5120) FLOOR", "mx_dim1_kernel", mx),
-            ("mx dequant (131072,5120)", "mx_dequant_kernel", mx)]
+            ("dim0_t (16640,8192) G=64 -> (8192,16640)", "dim0t_kernel", dim0(16640, 8192, 64)),
+            ("experts (16,5120,8192) along dim1", "dim0_kernel", 3 * 16 * 5120 * 8192 + 4 * 16 * 8192),
+            ("mx dim1 (131072,5120) FLOOR -> (5120,131072)", "mx_dim1_kernel", mx),
+            ("mx dequant (131072,5120) -> bf16", "mx_dequant_kernel", mx)]
 
 
 def _dispatches(path, name_col, reps, extra):
@@ -426,17 +436,21 @@ def counter_run(torch, mgs, wl, dev, reps):
         return lambda: f(x, o, pow2, q=q, scales=s)
 
     dim0, dim1 = mgs.mgs_quant_groups_dim0, mgs.mgs_quant_groups_dim1
+    g8 = torch.from_numpy(np.arange(1, 9, dtype=np.int32) * (x0.shape[0] // 8)).to(dev)
+    w3 = experts_weight(torch, dev)
+    q3, s3 = mgs.mgs_quant_experts_dim1(w3)
     q5, s5 = mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR)
     qt, st = mgs.mgs_quant_groups_dim0_t(x0, g64)
     qd1, sd1 = mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR)
     yd = mgs.mgs_mx_dequant_dim0(q5, s5)
     runs = [lambda: mgs.mgs_copy(src, dst),
-            grouped(dim0, x0, g64), grouped(dim0, x0, g1)] + \
+            grouped(dim0, x0, g64), grouped(dim0, x0, g1), grouped(dim0, x0, g8)] + \
         [grouped(dim0, x, o, p) for x, o, p in small] + \
         [grouped(dim1, x1, g64), grouped(dim1, x1, g16), grouped(dim1, x1, g1),
          lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_FLOOR, q=q5, scales=s5),
          lambda: mgs.mgs_mx_quant_dim0(x5, mgs.MGS_MX_RCEIL, q=q5, scales=s5),
          lambda: mgs.mgs_quant_groups_dim0_t(x0, g64, q_t=qt, scales_t=st),
+         lambda: mgs.mgs_quant_experts_dim1(w3, q=q3, scales=s3),
          lambda: mgs.mgs_mx_quant_dim1(x5, mgs.MGS_MX_FLOOR, q_t=qd1, scales_t=sd1),
          lambda: mgs.mgs_mx_dequant_dim0(q5, s5, y=yd)]
     assert len(runs) == len(counter_cases())
@@ -486,11 +500,31 @@ def steady_us(torch, fn, reps=20, lead=3):
     return a.elapsed_ms(b) * 1e3 / reps
 
 
-def per_config_table(torch, mgs, wl, dev, T, Tt, sha):
+def counter_traffic():
+    """Counter-run cases of profiles/hbm_traffic.json (label -> entry) when
+    they were taken on the current kernel sources, else {}."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        t = json.load(f)
+    return t.get("cases", {}) if t.get("source_hash") == kernel_source_hash() else {}
+
+
+# elements of each config's input that the oracle is timed on (about a third
+# of a second of one core); the rest of the config scales with it
+ORACLE_SAMPLE_ELEMS = 1 << 24
+
+
+def per_config_table(torch, mgs, wl, dev, T, Tt, sha, samples):
     """Per-config kernel times; records each generated input's sha256 in
-    `sha` (config name -> digest of x's bytes, then the offsets')."""
+    `sha` (config name -> digest of x's bytes, then the offsets'), and in
+    `samples` a slice of each grouped and MX config's input for the CPU
+    oracle's timing (config name -> (kind, slice, offsets or mode, pow2,
+    fraction of the config, algorithmic bytes of the config))."""
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
     rows = []
+    traffic = counter_traffic()
 
     def add(name, kind, x, off, bytes_, fn_maker, elems=None):
         fn = fn_maker()
@@ -507,11 +541,30 @@ def per_config_table(torch, mgs, wl, dev, T, Tt, sha):
             # the rowwise page's bytes convention: bf16 input counted twice
             # (2R + 1W + scales), for a like-for-like look at its table
             rows[-1]["page_convention_GBps"] = round((bytes_ + 2 * elems) / (med * 1e-6) / 1e9, 1)
+        if name in traffic:
+            # HBM bytes of this case from the rocprofv3 counter run, over this
+            # run's cold median
+            hb = traffic[name]["bytes_per_launch"]
+            rows[-1]["hbm_bytes_measured"] = hb
+            rows[-1]["measured_GBps"] = round(hb / (med * 1e-6) / 1e9, 1)
         log("  %-44s %9.2f us  %7.1f GB/s   back-to-back %9.2f us  %7.1f GB/s"
             % (name, med, rows[-1]["algorithmic_GBps"], sty, rows[-1]["steady_GBps"]))
 
+    def keep_sample(w):
+        M, K = w.x.shape
+        if w.kind == "dim0":      # every row of the first columns
+            n = min(K, max(8, ORACLE_SAMPLE_ELEMS // M // 8 * 8))
+            part = np.ascontiguousarray(w.x[:, :n])
+            frac = n / K
+        else:                     # the first rows
+            n = min(M, max(1, ORACLE_SAMPLE_ELEMS // K))
+            part = np.ascontiguousarray(w.x[:n])
+            frac = n / M
+        samples[w.name] = (w.kind, part, w.offsets, w.pow2, frac, w.algorithmic_bytes())
+
     def grouped(w):
         sha[w.name] = w.sha256()
+        keep_sample(w)
         x = torch.from_numpy(w.x.view(np.int16)).to(dev)
         o = torch.from_numpy(w.offsets).to(dev)
         f = mgs.mgs_quant_groups_dim0 if w.kind == "dim0" else mgs.mgs_quant_groups_dim1
@@ -544,8 +597,9 @@ def per_config_table(torch, mgs, wl, dev, T, Tt, sha):
     # per-expert scaling of a 3D weight along dim 1: 16 experts of (5120, 8192),
     # each expert a 5120-row group cut into 6-chunk teams (seeded on the GPU)
     E, D1, D2 = 16, 5120, 8192
-    gen = torch.Generator(device=dev).manual_seed(7)
-    w3 = (torch.randn((E, D1, D2), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    w3 = experts_weight(torch, dev)
+    sha["experts (16,5120,8192) bf16, torch seed 7"] = hashlib.sha256(
+        w3.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
     q3, s3 = mgs.mgs_quant_experts_dim1(w3)
     add("experts (16,5120,8192) along dim1", "experts", None, None, 3 * E * D1 * D2 + 4 * E * D2,
         lambda: (lambda: mgs.mgs_quant_experts_dim1(w3, q=q3, scales=s3)))
@@ -553,7 +607,10 @@ def per_config_table(torch, mgs, wl, dev, T, Tt, sha):
     c5 = wl.c5_mx()
     sha[c5.name + ", seed 5"] = c5.sha256()
     x5 = torch.from_numpy(c5.x.view(np.int16)).to(dev)
+    n_mx = ORACLE_SAMPLE_ELEMS // c5.x.shape[1]
     for mode, nm in ((mgs.MGS_MX_FLOOR, "FLOOR"), (mgs.MGS_MX_RCEIL, "RCEIL")):
+        samples[c5.name + " " + nm] = ("mx", np.ascontiguousarray(c5.x[:n_mx]), mode, False,
+                                        n_mx / c5.x.shape[0], c5.algorithmic_bytes())
         q, s = mgs.mgs_mx_quant_dim0(x5, mode)
         add(c5.name + " " + nm, "mx", c5.x, None, c5.algorithmic_bytes(),
             lambda: (lambda: mgs.mgs_mx_quant_dim0(x5, mode, q=q, scales=s)))
@@ -641,10 +698,12 @@ def host_call_cost(torch, mgs, wl, dev, n=2000):
     return rows
 
 
-def cpu_baseline(T, Tt, off, ncols):
+def cpu_baseline(T, Tt, off, ncols, samples):
     """The CPU oracle, untuned and single-threaded, on a bounded sample of
     the step: dim0 on T[:, :ncols] (every row, every group) and dim1 on the
-    first ncols rows of T^T. Throughput uses the same algorithmic bytes."""
+    first ncols rows of T^T. Throughput uses the same algorithmic bytes.
+    Then, per config, the oracle on the slice kept in `samples`, with the
+    whole config's time estimated from the slice's share of it."""
     import oracle
     from group_scaling_fp8_amd import workloads as wl
     xs0 = np.ascontiguousarray(T[:, :ncols])
@@ -657,9 +716,25 @@ def cpu_baseline(T, Tt, off, ncols):
     dt = time.perf_counter() - t0
     gbps = b / dt / 1e9
     log("cpu oracle: %.2f s on the sample, %.3f GB/s" % (dt, gbps))
+    per = []
+    for name, (kind, part, arg, pow2, frac, full_bytes) in samples.items():
+        t0 = time.perf_counter()
+        if kind == "dim0":
+            oracle.quant_groups_dim0(part, arg, pow2)
+        elif kind == "dim1":
+            oracle.quant_groups_dim1(part, arg, pow2)
+        else:
+            oracle.mx_quant_dim0(part, arg)
+        d = time.perf_counter() - t0
+        per.append({"config": name, "sample": "%s of %.2f%% of the input" % (
+                        "columns" if kind == "dim0" else "rows", 100 * frac),
+                    "sample_s": round(d, 3), "est_full_ms": round(1e3 * d / frac, 1),
+                    "GBps": round(full_bytes * frac / d / 1e9, 4)})
+        log("  cpu oracle %-36s %.3f s on %.2f%%, %.3f GB/s" % (name, d, 100 * frac, per[-1]["GBps"]))
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "dim0 on T[:, :%d] + dim1 on T^T[:%d] (%.1f%% of a step), %.2f s; host: %s, %d cpus"
-                      % (ncols, ncols, 100.0 * ncols / T.shape[1], dt, cpu_model(), os.cpu_count())}
+                      % (ncols, ncols, 100.0 * ncols / T.shape[1], dt, cpu_model(), os.cpu_count()),
+            "per_config": per}
 
 
 if __name__ == "__main__":
