@@ -338,7 +338,7 @@ int mgs_quant_groups_dim1(const void* x, int64_t M, int64_t K, const int32_t* of
     if (st != MGS_OK) return st;
     if (K % 16 != 0) return MGS_ERR_INVALID_ARG;
     if (K > MGS_DIM1_MAX_K) return MGS_ERR_UNSUPPORTED;
-    if (M == 0 || K == 0) return MGS_OK;
+    if (M == 0) return MGS_OK;
     if (!scales || !aligned(scales, 4)) return MGS_ERR_INVALID_ARG;
     if (flags & MGS_FLAG_VALIDATE) {
         st = validate_offsets(offsets, n_groups, K, 16, reinterpret_cast<hipStream_t>(stream));

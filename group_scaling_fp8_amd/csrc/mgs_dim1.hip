@@ -225,10 +225,26 @@ hipError_t launch_v(const uint16_t* x, int64_t M, int K, const int32_t* off, int
     return hipGetLastError();
 }
 
+// Rows of no columns: every group of every row is empty, so each of the
+// n = M * G scales is the amax = 0 value.
+__global__ __launch_bounds__(256) void empty_rows_kernel(float* __restrict__ scales, int64_t n,
+                                                          int pow2) {
+    const float s = group_scale(0u, pow2 != 0);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) scales[i] = s;
+}
+
 }  // namespace
 
 hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,
                        uint8_t* q, float* scales, int cus, hipStream_t stream) {
+    if (K == 0) {
+        const int64_t n = M * G;
+        const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+        hipLaunchKernelGGL(empty_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, scales, n,
+                           pow2 ? 1 : 0);
+        return hipGetLastError();
+    }
     const int nvec = K / 8;
     // Smallest V whose workgroup (a multiple of 64 threads) fits in 1024
     // threads; rows longer than 1024 * 4 vectors use V = 4 in column chunks.

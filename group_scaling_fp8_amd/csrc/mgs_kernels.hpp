@@ -30,6 +30,7 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
 // cus: compute units of the device; the grid is the workgroups that fit at once.
+// K == 0: only the scales are written (every group empty).
 hipError_t launch_dim1(const uint16_t* x, int64_t M, int K, const int32_t* off, int G, bool pow2,
                        uint8_t* q, float* scales, int cus, hipStream_t stream);
 

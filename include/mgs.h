@@ -239,8 +239,10 @@ int mgs_quant_experts_dim1(const void *w, int64_t E, int64_t D1, int64_t D2,
  *   q       (M, K) E4M3 bytes, written.
  *   scales  (M, n_groups) fp32, written. Empty groups get the amax = 0 value.
  * Requirements: K % 16 == 0, K <= MGS_DIM1_MAX_K (else MGS_ERR_UNSUPPORTED);
- * x 16-byte aligned, q 8-byte aligned, scales 4-byte aligned. M == 0 or
- * K == 0 is a no-op.
+ * x 16-byte aligned, q 8-byte aligned, scales 4-byte aligned. M == 0 is a
+ * no-op. K == 0 leaves every group empty: nothing is read and q is empty,
+ * but all M * n_groups scales are written with the amax = 0 value (x and q
+ * may then be NULL).
  */
 int mgs_quant_groups_dim1(const void *x, int64_t M, int64_t K,
                           const int32_t *offsets, int32_t n_groups,

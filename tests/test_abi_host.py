@@ -199,7 +199,10 @@ def test_mx_argument_errors(L):
 def test_noop_shapes_return_ok_without_gpu(L):
     # zero-sized work launches nothing, so these succeed even without a GPU
     assert L.mgs_quant_groups_dim1(None, 0, 128, A, 2, 0, None, None, None) == mgs.MGS_OK
-    assert L.mgs_quant_groups_dim1(None, 8, 0, A, 2, 0, None, None, None) == mgs.MGS_OK
+    assert L.mgs_quant_groups_dim1(None, 0, 0, A, 2, 0, None, None, None) == mgs.MGS_OK
+    # no columns but rows: the scales of the empty groups are still written
+    assert L.mgs_quant_groups_dim1(None, 8, 0, A, 2, 0, None, None, None) == INVALID
+    assert L.mgs_quant_groups_dim1(None, 8, 0, A, 2, 0, None, A + 2, None) == INVALID
     assert L.mgs_quant_groups_dim0(None, 8, 0, A, 2, 0, None, None, None) == mgs.MGS_OK
     assert L.mgs_mx_quant_dim0(None, 0, 64, None, 0, 0, None, None, None) == mgs.MGS_OK
     assert L.mgs_cast_e4m3(None, 0, None, None) == mgs.MGS_OK

@@ -174,6 +174,18 @@ def edge_values(rng, shape):
 
 
 @pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("M", [37, 300000])
+def test_dim1_no_columns_writes_scales(M, pow2):
+    # every group of every row is empty: all M * G scales get the amax = 0
+    # value (300000 rows: more scales than one pass of the fill's grid)
+    x = np.zeros((M, 0), np.uint16)
+    off = np.zeros(4, np.int32)
+    q, s = gpu_dim1(x, off, pow2)
+    _, rs = oracle.quant_groups_dim1(x, off, pow2)
+    assert_same_bytes(s, rs, "dim1 K=0 scales")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("M,K,sizes", [
     (1, 8, [1]),
     (40, 200, [0, 17, 0, 23, 0]),                # ragged strip (K % 128 != 0), empty groups
