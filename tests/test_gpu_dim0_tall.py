@@ -205,7 +205,7 @@ def test_graph_replays_with_the_library_workspace():
 def test_graph_keeps_its_workspace_when_the_stream_grows_its_own():
     """A graph captured on a stream keeps working after a later, larger eager
     call on that stream replaces the stream's workspace: the old buffer stays
-    alive, and the generation protocol needs nothing from the host."""
+    alive, and the workspace protocol needs nothing from the host."""
     M, K = 11000, 136
     off = np.array([200, 10600, 11000], np.int32)
     xs = [data(50 + i, M, K) for i in range(2)]
