@@ -59,36 +59,44 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const uint16_t* __restrict
 
 // ---- MX cast along dim0 (blocks of 32 rows), transposed output ------------------
 // The MX cast of x^T computed from x: q_t (K, M) E4M3 with blocks of 32 along
-// its rows and scales_t (K, M/32), the GEMM-ready form. A 256-thread workgroup
-// takes 128 rows x 128 columns; a lane holds 8 consecutive rows of 8 columns,
-// so each wave covers exactly one block of 32 rows and a column's block amax
-// is two lane swaps (the four lanes of the wave that share its columns). A
-// lane casts its 8 x 8 block and transposes it in registers; the tile goes
-// through 16 KiB of LDS so that q_t is written in whole 128-byte pieces of
-// its rows (eight lanes each), and the scales in runs of a column's blocks.
+// its rows and scales_t (K, M/32), the GEMM-ready form. A 1024-thread
+// workgroup takes 512 rows x 128 columns; a lane holds 8 consecutive rows of
+// 8 columns, so each wave covers exactly one block of 32 rows and a column's
+// block amax is two lane swaps (the four lanes of the wave that share its
+// columns). A lane casts its 8 x 8 block and transposes it in registers; the
+// tile goes through 64 KiB of LDS so that q_t is written in whole 512-byte
+// runs of its rows (32 lanes each), and the scales as a column's 16 blocks
+// in one 16-byte store. Taller tiles write longer runs of each q_t row:
+// 128 / 256 / 512 rows measured 378 / 371 / 364 us at (131072, 5120).
 // Tile order: each XCD (the dispatcher deals workgroups to the 8 XCDs in
-// turn) takes a contiguous run of tiles, M fastest. A tile writes 4 bytes
-// of each of its 128 scale rows; the 32 tiles that fill one 128-byte line of
+// turn) takes a contiguous run of tiles, M fastest. A tile writes 16 bytes
+// of each of its 128 scale rows; the 8 tiles that fill one 128-byte line of
 // a scale row then run on one XCD close together, so its L2 merges them and
-// writes whole lines (dealt in turn, every line was written in 4-byte
-// pieces from 8 L2s).
-constexpr int kMxTile = 128;
+// writes whole lines (dealt in turn, every line was written in pieces from
+// several L2s).
+constexpr int kMxRows = 512;                       // tile rows (M), a multiple of 32
+constexpr int kMxCols = 128;                       // tile columns (K)
+constexpr int kMxThreads = 2 * kMxRows;            // 16 lanes per 8 rows
+constexpr int kMxBlocks = kMxRows / 32;            // blocks of 32 rows per tile column
 constexpr int kXcds = 8;
+// the LDS word swizzle flips bits 2-4 of a word index inside a column of
+// kMxRows / 4 words, and four store passes cover 128 columns of kMxRows / 16 pieces
+static_assert(kMxRows % 128 == 0 && kMxThreads <= 1024, "mx_dim1 tile shape");
 
-__global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __restrict__ x, int64_t M,
+__global__ __launch_bounds__(kMxThreads) void mx_dim1_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                            int64_t K, int rceil,
                                                            uint8_t* __restrict__ q_t,
                                                            uint8_t* __restrict__ scales_t) {
-    const int64_t nm = (M + kMxTile - 1) / kMxTile;
+    const int64_t nm = (M + kMxRows - 1) / kMxRows;
     // workgroup b runs on XCD b % 8: the XCD's run of tiles starts at
     // x * (T / 8) + min(x, T % 8)
     const int64_t n_tiles = (int64_t)gridDim.x;
     const int64_t xcd = blockIdx.x % kXcds, k_in = blockIdx.x / kXcds;
     const int64_t tile = xcd * (n_tiles / kXcds) + min(xcd, n_tiles % kXcds) + k_in;
     const int64_t tile_m = tile % nm, tile_k = tile / nm;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;        // 16 column groups, 16 row groups
-    const int64_t row0 = tile_m * kMxTile + 8 * ty;                // this lane's 8 rows
-    const int64_t col = tile_k * kMxTile + 8 * tx;                  // and 8 columns
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;        // 16 column groups, 64 row groups
+    const int64_t row0 = tile_m * kMxRows + 8 * ty;                // this lane's 8 rows
+    const int64_t col = tile_k * kMxCols + 8 * tx;                  // and 8 columns
     // M % 32 == 0 and K % 8 == 0: a wave's block and a lane's columns are whole
     const bool ok = row0 < M && col < K;
     uint4 v[8];
@@ -125,9 +133,9 @@ __global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __res
     }
     // stage the cast tile in LDS as column words (four rows each), the word
     // index XOR-swizzled with the lane's column block, and the scale bytes as
-    // [column][block]; then store whole 128-byte pieces of q_t rows
-    __shared__ uint32_t st[kMxTile * kMxTile / 4];
-    __shared__ __attribute__((aligned(4))) uint8_t sst[kMxTile * 4];
+    // [column][block]; then store each column's run of its q_t row
+    __shared__ uint32_t st[kMxCols * kMxRows / 4];
+    __shared__ __attribute__((aligned(16))) uint8_t sst[kMxCols * kMxBlocks];
     const int w = threadIdx.x >> 6;                                 // this wave's block of the tile
     if (ok) {
         uint2 r[8];
@@ -142,25 +150,26 @@ __global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __res
         const int word = (2 * ty) ^ ((tx & 7) << 2);                // rows 8ty .. 8ty + 7
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<uint2*>(st + (8 * tx + j) * 32 + word) = make_uint2(lo03[j], lo47[j]);
-            *reinterpret_cast<uint2*>(st + (8 * tx + 4 + j) * 32 + word) = make_uint2(hi03[j], hi47[j]);
+            *reinterpret_cast<uint2*>(st + (8 * tx + j) * (kMxRows / 4) + word) = make_uint2(lo03[j], lo47[j]);
+            *reinterpret_cast<uint2*>(st + (8 * tx + 4 + j) * (kMxRows / 4) + word) = make_uint2(hi03[j], hi47[j]);
         }
         if ((ty & 3) == 0) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sst[(8 * tx + j) * 4 + w] = (uint8_t)byte[j];
+            for (int j = 0; j < 8; ++j) sst[(8 * tx + j) * kMxBlocks + w] = (uint8_t)byte[j];
         }
     }
     __syncthreads();
-    const int64_t r0 = tile_m * kMxTile, c0 = tile_k * kMxTile;
-    const int rows = (int)min((int64_t)kMxTile, M - r0);            // a multiple of 32
-    const int cols = (int)min((int64_t)kMxTile, K - c0);            // a multiple of 8
+    const int64_t r0 = tile_m * kMxRows, c0 = tile_k * kMxCols;
+    const int rows = (int)min((int64_t)kMxRows, M - r0);            // a multiple of 32
+    const int cols = (int)min((int64_t)kMxCols, K - c0);            // a multiple of 8
     const int pieces = rows >> 4;                                    // 16-byte pieces per column
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int idx = threadIdx.x + k * kThreads;                  // 8 pieces per column, pieces fastest
-        const int c = idx >> 3, p = idx & 7;
+        const int idx = threadIdx.x + k * kMxThreads;                // 32 pieces per column, pieces fastest
+        const int c = idx / (kMxRows / 16), p = idx % (kMxRows / 16);
         if (c < cols && p < pieces) {
-            const uint4 val = *reinterpret_cast<const uint4*>(st + c * 32 + ((4 * p) ^ (((c >> 3) & 7) << 2)));
+            const uint4 val =
+                *reinterpret_cast<const uint4*>(st + c * (kMxRows / 4) + ((4 * p) ^ (((c >> 3) & 7) << 2)));
             store_stream16(q_t + (c0 + c) * M + r0 + 16 * p, val);
         }
     }
@@ -168,11 +177,11 @@ __global__ __launch_bounds__(kThreads) void mx_dim1_kernel(const uint16_t* __res
         const int c = threadIdx.x;
         const int64_t nb = M / 32;
         uint8_t* dst = scales_t + (c0 + c) * nb + r0 / 32;
-        if (rows == kMxTile && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
-            // the column's four blocks in one 4-byte store
-            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(sst + c * 4);
+        if (rows == kMxRows && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            // the column's 16 blocks in one 16-byte store
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(sst + c * kMxBlocks);
         } else {
-            for (int b = 0; b < (rows >> 5); ++b) dst[b] = sst[c * 4 + b];
+            for (int b = 0; b < (rows >> 5); ++b) dst[b] = sst[c * kMxBlocks + b];
         }
     }
 }
@@ -281,9 +290,9 @@ hipError_t launch_mx(const uint16_t* x, int64_t n_elems, bool rceil, uint8_t* q,
 
 hipError_t launch_mx_dim1(const uint16_t* x, int64_t M, int64_t K, bool rceil, uint8_t* q_t,
                           uint8_t* scales_t, hipStream_t stream) {
-    const int64_t tiles = ((M + kMxTile - 1) / kMxTile) * ((K + kMxTile - 1) / kMxTile);
+    const int64_t tiles = ((M + kMxRows - 1) / kMxRows) * ((K + kMxCols - 1) / kMxCols);
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mx_dim1_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, x, M, K,
+    hipLaunchKernelGGL(mx_dim1_kernel, dim3((unsigned)tiles), dim3(kMxThreads), 0, stream, x, M, K,
                        rceil ? 1 : 0, q_t, scales_t);
     return hipGetLastError();
 }
