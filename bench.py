@@ -8,10 +8,10 @@ are the two halves of the shape the rowwise page benchmarks ("[moe fp8
 training] test and bench new faster method for per group rowwise scaling",
 Benchmarks table, (16640, 8192) with 64 groups).
 
-The single JSON line on stdout keeps the driver's contract: `value` is the
-algorithmic HBM throughput of the whole step (read bf16 once, write E4M3
-once, write fp32 scales, read offsets) over the timed steps, with every input
-already resident in HBM. `roofline` reports the slower of the two kernels
+The single JSON line on stdout: `value` is the algorithmic HBM throughput of
+the whole step (read bf16 once, write E4M3 once, write fp32 scales, read
+offsets) over the timed steps, with every input already resident in HBM and
+the GPU brought to steady clocks by 30 ms of untimed steps first. `roofline` reports the slower of the two kernels
 against MI355X's 8 TB/s, timed with HIP events on the stream the library
 launches on. `cpu_baseline` times the CPU oracle on a bounded sample of the
 same step. Per-config kernel times (each run after a cache flush) go into
