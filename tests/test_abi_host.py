@@ -222,3 +222,34 @@ def test_python_binding_rejects_cpu_tensors():
     off = torch.tensor([16], dtype=torch.int32)
     with pytest.raises(ValueError):
         mgs.mgs_quant_groups_dim0(x, off)
+
+
+def test_missing_library_fails_loudly():
+    """Without libmgs.so the binding raises on first use: there is no CPU
+    fallback to route the work through."""
+    import subprocess
+    import sys
+    code = ("import group_scaling_fp8_amd._lib as L\n"
+            "L._LIB_PATH = '/nonexistent/libmgs.so'\n"
+            "try:\n    L.lib()\nexcept RuntimeError as e:\n    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert "raised: libmgs.so not found" in r.stdout, r.stdout + r.stderr
+
+
+def test_product_path_never_imports_the_oracle():
+    """The package (the binding and its helpers) imports nothing from
+    oracle/: the oracle is test infrastructure only."""
+    import ast
+    pkg = os.path.join(ROOT, "group_scaling_fp8_amd")
+    for name in sorted(os.listdir(pkg)):
+        if not name.endswith(".py"):
+            continue
+        tree = ast.parse(open(os.path.join(pkg, name)).read())
+        for node in ast.walk(tree):
+            if isinstance(node, ast.Import):
+                mods = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                mods = [node.module or ""]
+            else:
+                continue
+            assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), (name, mods)
