@@ -388,3 +388,43 @@ def test_validate_flag():
         with pytest.raises(mgs.MgsError) as e:
             mgs.mgs_quant_groups_dim1(xt, to_dev(np.array(off, np.int32)), validate=True)
         assert e.value.status == mgs.MGS_ERR_INVALID_ARG, off
+
+
+# ------------------------------------------------ outliers at group edges
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_outliers_at_group_edges(pow2):
+    """The largest magnitude of every group sits in its first or last row
+    (dim0, dim0_t) or column (dim1), with small values elsewhere. A group
+    boundary off by one would put an outlier into the neighbouring group's
+    amax and change that group's scales."""
+    rng = np.random.default_rng(4242)
+    # dim0 / dim0_t: 16-aligned boundaries (dim0_t's requirement), groups of
+    # 16 rows to tall chunked ones, and empty groups
+    sizes = np.array([16, 0, 48, 1024, 16, 0, 2048, 32, 112, 3200], np.int64)
+    off = np.cumsum(sizes).astype(np.int32)
+    M, K = int(off[-1]), 264
+    x = wl.randn_bf16(rng, (M, K), 0.02)
+    start = 0
+    for g, n in enumerate(sizes):
+        if n:
+            edge = start if g % 2 == 0 else start + n - 1
+            big = wl.f32_to_bf16_bits(np.float32(rng.choice([-1.0, 1.0]) * (8.0 + g)))
+            x[edge, :] = big
+        start += n
+    check_dim0(x, off, pow2, "dim0 edge outliers")
+    q_t, s_t = mgs.mgs_quant_groups_dim0_t(to_dev(x), to_dev(off), pow2)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_groups_dim0_t(x, off, pow2)
+    assert_same_bytes(s_t.cpu().numpy(), rs, "dim0_t edge outliers scales")
+    assert_same_bytes(q_t.cpu().numpy(), rq, "dim0_t edge outliers q")
+    # dim1: the same along the columns of 40 rows
+    xs = wl.randn_bf16(rng, (40, M), 0.02)
+    start = 0
+    for g, n in enumerate(sizes):
+        if n:
+            edge = start if g % 2 == 0 else start + n - 1
+            xs[:, edge] = wl.f32_to_bf16_bits(np.float32(-(8.0 + g)))
+        start += n
+    check_dim1(xs, off, pow2, "dim1 edge outliers")
