@@ -11,11 +11,12 @@ Benchmarks table, (16640, 8192) with 64 groups).
 The single JSON line on stdout: `value` is the algorithmic HBM throughput of
 the whole step (read bf16 once, write E4M3 once, write fp32 scales, read
 offsets) over the timed steps, with every input already resident in HBM and
-the GPU brought to steady clocks by 30 ms of untimed steps first. `roofline` reports the slower of the two kernels
-against MI355X's 8 TB/s, timed with HIP events on the stream the library
-launches on. `cpu_baseline` times the CPU oracle on a bounded sample of the
-same step. Per-config kernel times (each run after a cache flush) go into
-`kernels`. Human-readable detail goes to stderr.
+the GPU brought to steady clocks by 50 ms of untimed steps first.
+`roofline` reports the slower of the two kernels against MI355X's 8 TB/s,
+timed with HIP events on the stream the library launches on.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+Per-config kernel times (each run after a cache flush) go into `kernels`.
+Human-readable detail goes to stderr.
 """
 import argparse
 import hashlib
@@ -296,7 +297,7 @@ KERNELS = (("copy_kernel", "copy"), ("mx_dim1_kernel", "mx_dim1_kernel"),
            ("mx_dequant_kernel", "mx_dequant_kernel"), ("mx_kernel", "mx_kernel"),
            ("zero_kernel", "zero_kernel"), ("dim0t_kernel", "dim0t_kernel"),
            ("dim0_kernel", "dim0_kernel"), ("dim1_kernel", "dim1_kernel"))
-PREWARM_MS = 30.0          # untimed steps before the warmup steps (clock settling)
+PREWARM_MS = 50.0          # untimed steps before the warmup steps (clock settling)
 COPY_BYTES = 1 << 28      # the counter run's calibration copy: 256 MiB read + 256 MiB written
 
 
