@@ -26,11 +26,18 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every HIP source into group_scaling_fp8_amd/libmgs.so."""
+LIB_TRACE = os.path.join(PKG, "libmgs_trace.so")
+
+
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compiles every HIP source into group_scaling_fp8_amd/libmgs.so; with
+    trace=True into libmgs_trace.so instead, the same library with the dim0
+    tile timeline recorded (MGS_TILE_TRACE, a diagnostic)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + sources()
+    out = LIB_TRACE if trace else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc] + HIPCC_FLAGS + (["-DMGS_TILE_TRACE"] if trace else []) + \
+        ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + sources()
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,9 +48,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, err))
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv[1:]))

@@ -63,8 +63,28 @@
 // of a strip together; class C chunk by chunk with strips fastest.
 #include "mgs_device.hpp"
 #include "mgs_kernels.hpp"
+#if defined(MGS_TILE_TRACE)
+#include "mgs_trace.h"
+#endif
 
 namespace mgs {
+
+#if defined(MGS_TILE_TRACE)
+// Tile timeline, in trace builds only (libmgs_trace.so). For each tile item
+// i < kTraceTiles that casts (column-maximum tiles of class C are not
+// recorded), eight 64-bit words: five s_memrealtime stamps (100 MHz) at the
+// item's start, the tile found, its loads and column maxima done (a team
+// tile: after the team's maxima came in; a class C casting tile: after its
+// strip's maxima came in and its loads), the reduction across the workgroup
+// done, and its stores issued; then the workgroup's placement (HW_ID << 32 |
+// XCC_ID), class << 60 | chunk << 32 | rows, and group << 40 | strip << 16 |
+// strip width in columns. Each launch overwrites the items it runs.
+constexpr int kTraceTiles = 16384;
+__device__ unsigned long long g_tile_trace[kTraceTiles * 8];
+#define MGS_TRACE_STAMP(v) const unsigned long long v = __builtin_amdgcn_s_memrealtime()
+#else
+#define MGS_TRACE_STAMP(v)
+#endif
 
 namespace {
 
@@ -577,11 +597,13 @@ __device__ __forceinline__ void dim0_body(
     const unsigned stride = xcd_split ? gridDim.x >> 3 : gridDim.x;
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = first; item < (unsigned)n_tiles; item += stride) {
+        MGS_TRACE_STAMP(tr0);
         Tile t = find_tile<kRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign, uniform_rows,
                                        (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         t.strip += xcol * (Ks >> (t.lt + 3));
         const TileGeom geo = tile_geom(t, K);
+        MGS_TRACE_STAMP(tr1);
         const int nrows = t.r1 - t.r0;      // at most the register capacity in every class
         // a team: the tiles of one chunked group on one strip (class C: its
         // column-maximum tiles too), with one counter in the workspace
@@ -654,7 +676,9 @@ __device__ __forceinline__ void dim0_body(
                 if (wave0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
         }
+        MGS_TRACE_STAMP(tr2);
         m = block_column_amax(m, geo.tpr, red);
+        MGS_TRACE_STAMP(tr3);
 
         // every lane derives its own 8 scales; lanes of row 0 store them
         const bool p2 = pow2 != 0;
@@ -754,6 +778,24 @@ __device__ __forceinline__ void dim0_body(
                 }
             }
         }
+#if defined(MGS_TILE_TRACE)
+        if (threadIdx.x == 0 && item < (unsigned)kTraceTiles) {
+            MGS_TRACE_STAMP(tr4);
+            unsigned hw, xcc;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+            unsigned long long* d = g_tile_trace + 8 * (size_t)item;
+            d[0] = tr0;
+            d[1] = tr1;
+            d[2] = tr2;
+            d[3] = tr3;
+            d[4] = tr4;
+            d[5] = ((unsigned long long)hw << 32) | xcc;
+            d[6] = ((unsigned long long)t.cls << 60) | ((unsigned long long)t.c << 32) | (unsigned)nrows;
+            d[7] = ((unsigned long long)t.g << 40) | ((unsigned long long)t.strip << 16) |
+                   (unsigned)(8 << t.lt);
+        }
+#endif
         uint32_t before = 0;
         if (chunked && wave0) before = team_tile_done(team_ctr, team_size);
         __syncthreads();     // red (and the stage) are rewritten by the next item
@@ -832,3 +874,41 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
 }
 
 }  // namespace mgs
+
+#if defined(MGS_TILE_TRACE)
+// Trace builds only: the tile timeline of the last dim0-family launches (see
+// g_tile_trace). Return hipError_t codes.
+extern "C" int mgs_tile_trace_capacity(void) { return mgs::kTraceTiles; }
+
+extern "C" int mgs_tile_trace_clear(void) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(mgs::g_tile_trace));
+    if (e != hipSuccess) return (int)e;
+    e = hipMemset(p, 0, sizeof(mgs::g_tile_trace));
+    if (e != hipSuccess) return (int)e;
+    return (int)hipDeviceSynchronize();
+}
+
+namespace mgs {
+namespace {
+__global__ void tile_trace_stamp_kernel(unsigned long long* dst) {
+    if (threadIdx.x == 0) *dst = __builtin_amdgcn_s_memrealtime();
+}
+}  // namespace
+}  // namespace mgs
+
+extern "C" int mgs_tile_trace_stamp(void* dst, void* stream) {
+    if (!dst || (reinterpret_cast<uintptr_t>(dst) & 7)) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mgs::tile_trace_stamp_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<unsigned long long*>(dst));
+    return (int)hipGetLastError();
+}
+
+extern "C" int mgs_tile_trace_read(void* dst, int64_t bytes) {
+    if (!dst || bytes < 0 || (size_t)bytes > sizeof(mgs::g_tile_trace)) return (int)hipErrorInvalidValue;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return (int)e;
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(mgs::g_tile_trace), (size_t)bytes, 0,
+                                    hipMemcpyDeviceToHost);
+}
+#endif

@@ -38,6 +38,31 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(mgs._lib.EXPORTS)
 
 
+def test_trace_build_exports(L):
+    """libmgs_trace.so (the tile-timeline diagnostic build) exports every
+    entry point of mgs.h plus the calls of mgs_trace.h; libmgs.so exports
+    none of the latter."""
+    from group_scaling_fp8_amd import build
+    if not os.path.exists(build.LIB_TRACE):
+        build.build(trace=True)
+    T = ctypes.CDLL(build.LIB_TRACE)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mgs_trace.h")).read(), flags=re.S)
+    trace_names = set(re.findall(r"^\s*\w+\s*\*?\s*(mgs_\w+)\s*\(", text, flags=re.M))
+    assert trace_names == {"mgs_tile_trace_capacity", "mgs_tile_trace_clear", "mgs_tile_trace_read",
+                           "mgs_tile_trace_stamp"}
+    for n in header_functions() + sorted(trace_names):
+        assert hasattr(T, n), n
+    for n in trace_names:
+        assert not hasattr(L, n), n
+    T.mgs_tile_trace_capacity.restype = ctypes.c_int
+    assert T.mgs_tile_trace_capacity() == 16384
+    # argument checks come before any HIP call
+    T.mgs_tile_trace_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    T.mgs_tile_trace_stamp.restype = ctypes.c_int
+    assert T.mgs_tile_trace_stamp(None, None) != 0
+    assert T.mgs_tile_trace_stamp(A + 4, None) != 0
+
+
 def test_status_strings(L):
     for code in range(4):
         assert L.mgs_status_string(code)
