@@ -21,7 +21,7 @@ import pytest
 CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                     "group_scaling_fp8_amd", "csrc")
 
-DRIVER = r"""
+BOUND_PROGRAM = r"""
 #include <stdio.h>
 #include "mgs_dim0_layout.hpp"
 int main() {
@@ -85,7 +85,7 @@ def bound_tool():
     src = os.path.join(d, "bound.cpp")
     exe = os.path.join(d, "bound")
     with open(src, "w") as f:
-        f.write(DRIVER)
+        f.write(BOUND_PROGRAM)
     subprocess.run(["g++", "-O1", "-std=c++17", "-I", CSRC, "-o", exe, src], check=True)
 
     def run(triples):
