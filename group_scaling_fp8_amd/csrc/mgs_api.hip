@@ -255,8 +255,7 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
                                        n_groups, (int)uniform_rows,
                                        (flags & MGS_FLAG_POW2_SCALE) != 0, transposed,
                                        static_cast<uint8_t*>(q), scales, team_max, lt_cap, xcd_split, w,
-                                       spin_ticks,
-                                       s));
+                                       spin_ticks, dinfo.cus, s));
 }
 
 int quant_experts(const void* w, int64_t E, int64_t D1, int64_t D2, uint32_t flags, void* q,

@@ -63,6 +63,9 @@
 // of a strip together; class C chunk by chunk with strips fastest.
 #include "mgs_device.hpp"
 #include "mgs_kernels.hpp"
+
+#include <map>
+#include <mutex>
 #if defined(MGS_TILE_TRACE)
 #include "mgs_trace.h"
 #endif
@@ -841,16 +844,50 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_
         p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Workgroups of dim0_kernel the device holds at once (two per CU by design:
+// 72 KiB of LDS and at most 128 VGPRs each), from the runtime's occupancy
+// query, kept per device; 0 if the query fails.
+int dim0_resident(int cus) {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(dev);
+        if (it != cache.end()) return it->second;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dim0_kernel, kThreads, 0) != hipSuccess ||
+            per_cu < 1)
+        return 0;
+    const int resident = per_cu * (cus > 0 ? cus : 1);
+    std::lock_guard<std::mutex> lock(mu);
+    cache[dev] = resident;
+    return resident;
+}
+
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
                        bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
-                       bool xcd_split, void* ws, long long spin_ticks, hipStream_t stream) {
+                       bool xcd_split, void* ws, long long spin_ticks, int cus, hipStream_t stream) {
     const int64_t chunk_rows = transposed ? kDim0ChunkRowsT : kDim0ChunkRows;
     // with xcd_split every XCD runs the tiling of K / 8 columns
     const int64_t n_tiles = dim0_tile_bound(M, xcd_split ? K / 8 : K, G, team_max, lt_cap, chunk_rows);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
     const int64_t per = n_tiles < (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid)
                             ? n_tiles : (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid);
-    const int64_t grid = xcd_split ? 8 * per : per;
+    int64_t grid = xcd_split ? 8 * per : per;
+    // One to three rounds of tiles (by the bound): one resident round of
+    // workgroups instead, each walking its tiles b, b + grid, ... with no
+    // exit, dispatch and start between them. With more rounds, one
+    // workgroup per tile lets the hardware dispatcher balance tiles of
+    // unequal size; a fixed share of them was slower there. Teams stay
+    // consecutive in the tile order and hold fewer tiles than the grid, so
+    // the lowest tile in progress always has every teammate started or done.
+    if (!transposed && !xcd_split) {
+        const int resident = dim0_resident(cus);
+        if (resident > 0 && grid > resident && grid <= 3 * (int64_t)resident) grid = resident;
+    }
     const Dim0Workspace w = dim0_workspace(M, K);
     char* base = static_cast<char*>(ws);
     uint32_t* ws_ctr = base ? reinterpret_cast<uint32_t*>(base + w.ctr_off) : nullptr;

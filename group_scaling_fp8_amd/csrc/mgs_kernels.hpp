@@ -21,10 +21,11 @@ namespace mgs {
 // are rounded down to them). xcd_split: XCD x (workgroups x, x + 8, ...)
 // takes the tiles of columns [x K/8, (x + 1) K/8); K / 8 must be a multiple
 // of the widest strip, 8 << lt_cap columns, and team_max at most the
-// workgroups one XCD holds at once, halved (dim0_xcd_split).
+// workgroups one XCD holds at once, halved (dim0_xcd_split). cus: the
+// device's compute units (sizes the resident grid of few-round launches).
 hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int G, int uniform_rows,
                        bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
-                       bool xcd_split, void* ws, long long spin_ticks, hipStream_t stream);
+                       bool xcd_split, void* ws, long long spin_ticks, int cus, hipStream_t stream);
 
 // Zero fill of bytes / 16 16-byte words at p (16-byte aligned) by a kernel.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);

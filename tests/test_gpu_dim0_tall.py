@@ -8,8 +8,9 @@ forced low here through the test-only entry point's team limit), the path
 that computes those maxima from x in the waiting tile itself (forced from
 the host by a negative wait bound), back-to-back calls on one stream and on
 two, the library's own workspace and caller-owned ones (which every call
-leaves zero-filled), replays of captured graphs, and teams beside other
-kernels."""
+leaves zero-filled), replays of captured graphs, teams beside other
+kernels, and launches of a few rounds of tiles, which run as one resident
+round of workgroups."""
 import numpy as np
 import pytest
 import torch
@@ -127,6 +128,20 @@ def test_tall_groups_without_the_wait(M, K, sizes, team_max):
     x = data(M + K, M, K)
     check(x, off, "no wait %s" % (sizes,), team_max=team_max, spin=-1)
     check(x, off, "zero wait %s" % (sizes,), team_max=team_max, spin=0)
+
+
+# Launches of one to three rounds of tiles (by the grid bound; (16640, 4096)
+# gives 608 to 1478 here) run as one resident round of workgroups, each
+# walking its tiles. At G=1 a 19-chunk team straddles the first round
+# (tiles 494-512); with a team limit of 4 the column-maximum tiles come
+# first and the casting tiles wait for maxima written in the same or an
+# earlier pass of the resident workgroups.
+@pytest.mark.parametrize("team_max", [None, 4])
+@pytest.mark.parametrize("sizes", [[16640], [6000, 10640], [0, 9000, 7640]])
+def test_resident_grid_launches(sizes, team_max):
+    off = np.cumsum(sizes).astype(np.int32)
+    x = data(len(sizes) + 77, 16640, 4096)
+    check(x, off, "resident grid %s" % (sizes,), team_max=team_max)
 
 
 @pytest.mark.parametrize("team_max", TEAM_MAX)
