@@ -28,8 +28,10 @@
 // teams. A tile is rows of one group times a strip of 8 * tpr columns, tpr
 // lanes per row:
 //   * class A, R <= C rows: one tile per strip. tpr is the widest power of
-//     two in [16, 128] whose tile fits (short groups get strips up to 1024
-//     columns). Load -> column amax -> scale -> cast from registers -> store.
+//     two in [16, 512] whose tile fits (short groups get strips up to 4096
+//     columns; up to 1024 in the transposed kernel, whose LDS stage holds
+//     strips of at most that width). Load -> column amax -> scale -> cast
+//     from registers -> store.
 //     No strip is narrower than 128 columns unless K is, or the launch would
 //     otherwise have fewer tiles than CUs (lt_cap, from dim0_lt_cap): rows of
 //     128 bytes stream far worse than rows of 256.
@@ -111,7 +113,7 @@ struct Tile {
     int g;          // group, or -1 when this workgroup has no tile
     int maxima;     // 1: class C column-maximum tile (writes no output)
     int cls;        // kClassA / kClassT / kClassC
-    int lt;         // log2 of lanes per row (3..7)
+    int lt;         // log2 of lanes per row (3..9)
     int strip;      // column strip index (strip width 8 << lt)
     int c, nc;      // chunk index and chunk count (classes T, C), else 0 and 1
     int r0, r1;     // rows of this tile (the chunk for classes T, C)
@@ -140,7 +142,8 @@ __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, 
         gi.nc = (R + kRows - 1) / kRows;
         gi.cls = gi.nc <= team_max ? kClassT : kClassC;
     } else {
-        gi.lt = R <= kRows / 8 ? 7 : (R <= kRows / 4 ? 6 : (R <= kRows / 2 ? 5 : 4));
+        gi.lt = R <= kRows / 32 ? 9 : (R <= kRows / 16 ? 8 : (R <= kRows / 8 ? 7 :
+                (R <= kRows / 4 ? 6 : (R <= kRows / 2 ? 5 : 4))));
         gi.cls = kClassA;
     }
     // no strip wider than needed to cover K

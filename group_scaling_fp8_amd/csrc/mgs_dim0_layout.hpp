@@ -38,8 +38,8 @@ inline int64_t dim0_chunk_bound(int64_t M, int64_t chunk_rows) {
 
 // Tiles of one group of R rows (the rule of the kernel's tile search), with
 // C = chunk_rows: n(w) = ceil(K / w') strips of width w' = min(w, 8 << max_lt)
-// with w = 1024 columns for R <= C/8, 512 up to C/4, 256 up to C/2 and 128
-// up to C. A taller group has c = ceil(R / C) chunks on n(128) strips:
+// with w = 4096 columns for R <= C/32, 2048 up to C/16, 1024 up to C/8, 512
+// up to C/4, 256 up to C/2 and 128 up to C. A taller group has c = ceil(R / C) chunks on n(128) strips:
 // c * n(128) tiles as a team (c <= team_max), else 2 * c * n(128).
 inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max, int max_lt,
                                 int64_t chunk_rows) {
@@ -48,6 +48,8 @@ inline int64_t dim0_group_tiles(int64_t R, int64_t K, int64_t team_max, int max_
         const int64_t wc = w < wmax ? w : wmax;
         return (K + wc - 1) / wc;
     };
+    if (R <= chunk_rows / 32) return n(4096);
+    if (R <= chunk_rows / 16) return n(2048);
     if (R <= chunk_rows / 8) return n(1024);
     if (R <= chunk_rows / 4) return n(512);
     if (R <= chunk_rows / 2) return n(256);
@@ -79,6 +81,8 @@ inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max
         const int64_t e = M * num / first_rows;
         if (e > extra) extra = e;
     };
+    step(chunk_rows / 32 + 1);
+    step(chunk_rows / 16 + 1);
     step(chunk_rows / 8 + 1);
     step(chunk_rows / 4 + 1);
     step(chunk_rows / 2 + 1);
@@ -90,8 +94,9 @@ inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max
     return spread < one ? spread : one;
 }
 
-// Widest strips the launch may use (log2 of 8-column units per strip, 3..7).
-// Never wider than K needs. A tiny problem also gets narrower strips, down
+// Widest strips the launch may use (log2 of 8-column units per strip, 3..9;
+// at most 7, 1024 columns, for the transposed kernel, chunk_rows =
+// kDim0ChunkRowsT). Never wider than K needs. A tiny problem also gets narrower strips, down
 // to 64 columns, until G groups of M / G rows would make at least one tile
 // per CU: otherwise a handful of tiles leaves most CUs idle. Only then:
 // strips under 256 bytes of bf16 per row stream poorly, and problems with a
@@ -99,7 +104,8 @@ inline int64_t dim0_tile_bound(int64_t M, int64_t K, int64_t G, int64_t team_max
 inline int dim0_lt_cap(int64_t M, int64_t K, int64_t G, int64_t team_max, int64_t cus,
                        int64_t chunk_rows) {
     int lt = 3;
-    while (lt < 7 && (int64_t(8) << lt) < K) ++lt;
+    const int max_lt = chunk_rows == kDim0ChunkRowsT ? 7 : 9;
+    while (lt < max_lt && (int64_t(8) << lt) < K) ++lt;
     if (G < 1) return lt;
     const int64_t want = cus;
     while (lt > 3 && G * dim0_group_tiles(M / G, K, team_max, lt, chunk_rows) < want) --lt;

@@ -114,8 +114,9 @@ def test_grouped_argument_errors(L, fn):
     if fn.endswith("dim0") or fn.endswith("dim0_ws") or fn.endswith("_noalloc"):
         assert call(K=12) == INVALID
         assert call(s=A + 4) == INVALID
-        # 1024 groups of 1024-column strips over K = 2^31 - 8: the tile bound reaches 2^31
-        assert call(K=(1 << 31) - 8, G=1024) == UNSUPPORTED
+        # 1024 groups over 65536 rows of K = 2^31 - 8 columns (taller groups
+        # cut into chunk teams on 128-column strips): the tile bound passes 2^31
+        assert call(M=65536, K=(1 << 31) - 8, G=1024) == UNSUPPORTED
     elif fn.endswith("dim0_t"):
         assert call(K=12) == INVALID
         assert call(M=24) == INVALID            # M % 16

@@ -4,9 +4,9 @@ The dim0 launch has one workgroup per tile and sizes its grid from (M, K, G)
 alone, so the bound must hold for every way of splitting M rows into G
 groups. The tile count of a group depends only on its row count, as a step
 function, so the worst split is found exactly by a knapsack over the first
-row count of each step (0, C/8 + 1, C/4 + 1, C/2 + 1, then C * (c - 1) + 1
-for the groups cut into c >= 2 chunks, with C the chunk rows: 896 for the
-dim0 kernel, 640 for the transposed one). The C++ bound, compiled with g++
+row count of each step (0, C/32 + 1, C/16 + 1, C/8 + 1, C/4 + 1, C/2 + 1,
+then C * (c - 1) + 1 for the groups cut into c >= 2 chunks, with C the chunk
+rows: 896 for the dim0 kernel, 640 for the transposed one). The C++ bound, compiled with g++
 from the header the library uses, must be at least that worst case, for
 several team limits (the most chunks a group may have to be cast as a
 team)."""
@@ -41,6 +41,7 @@ int main() {
 
 
 CHUNKS = [896, 640]      # chunk rows of the dim0 and dim0_t kernels
+WIDEST = {896: 9, 640: 7}   # their widest strips: 4096 and 1024 columns
 
 
 def tiles(R, K, team_max, max_lt=7, C=896):
@@ -49,7 +50,8 @@ def tiles(R, K, team_max, max_lt=7, C=896):
     if R > C:
         lt, chunks = 4, -(-R // C)
     else:
-        lt = 7 if R <= C // 8 else 6 if R <= C // 4 else 5 if R <= C // 2 else 4
+        lt = (9 if R <= C // 32 else 8 if R <= C // 16 else 7 if R <= C // 8 else
+              6 if R <= C // 4 else 5 if R <= C // 2 else 4)
         chunks = 0
     lt = min(lt, max_lt)
     while lt > 3 and (8 << (lt - 1)) >= K:
@@ -63,7 +65,8 @@ def tiles(R, K, team_max, max_lt=7, C=896):
 def worst_splits(Mmax, K, Gmax, team_max, max_lt=7, C=896):
     """best[G][M] = the most tiles over all splits of at most M rows into
     exactly G groups."""
-    sizes = [0, C // 8 + 1, C // 4 + 1, C // 2 + 1] + [C * (c - 1) + 1 for c in range(2, Mmax // C + 3)]
+    sizes = [0, C // 32 + 1, C // 16 + 1, C // 8 + 1, C // 4 + 1, C // 2 + 1] + \
+        [C * (c - 1) + 1 for c in range(2, Mmax // C + 3)]
     sizes = [r for r in sizes if r <= Mmax]
     NEG = -(1 << 40)
     dp = np.full(Mmax + 1, NEG, np.int64)
@@ -97,31 +100,33 @@ def bound_tool():
 
 @pytest.mark.parametrize("C", CHUNKS)
 @pytest.mark.parametrize("team_max", [1, 3, 26, 128])
-@pytest.mark.parametrize("K", [8, 64, 72, 136, 1032, 8192])
+@pytest.mark.parametrize("K", [8, 64, 72, 136, 1032, 2056, 4104, 8192])
 def test_bound_covers_the_worst_split(bound_tool, K, team_max, C):
     Mmax, Gmax = 17000, 64
-    best = worst_splits(Mmax, K, Gmax, team_max, 7, C)
-    Ms = [0, 1, 80, 81, 113, 400, 449, 640, 641, 896, 897, 1280, 1281, 1793, 1921, 5120, 5121, 6000,
-          10242, 12000, 16640, 17000]
+    lt = WIDEST[C]
+    best = worst_splits(Mmax, K, Gmax, team_max, lt, C)
+    Ms = [0, 1, 20, 21, 28, 29, 40, 41, 56, 57, 80, 81, 113, 400, 449, 640, 641, 896, 897, 1280, 1281,
+          1793, 1921, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
     Gs = [1, 2, 3, 7, 16, 64]
-    triples = [(M, K, G, team_max, 7, C) for M in Ms for G in Gs]
+    triples = [(M, K, G, team_max, lt, C) for M in Ms for G in Gs]
     got = bound_tool(triples)
     for (M, _, G, _, _, _), (b, _, one) in zip(triples, got):
         exact = int(best[G][M])
         assert b >= exact, (M, K, G, team_max, C, b, exact)
         # and it is no wild over-estimate (the grid's extra workgroups exit at once)
         assert b <= 2 * exact + 16, (M, K, G, team_max, C, b, exact)
-        assert one == tiles(M, K, team_max, 7, C)
+        assert one == tiles(M, K, team_max, lt, C)
 
 
 @pytest.mark.parametrize("C", CHUNKS)
-@pytest.mark.parametrize("max_lt", [3, 4, 5, 6])
-@pytest.mark.parametrize("K", [64, 1032, 4096])
+@pytest.mark.parametrize("max_lt", [3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("K", [64, 1032, 4096, 8200])
 def test_bound_with_narrowed_strips(bound_tool, K, max_lt, C):
     team_max = 128
     Mmax, Gmax = 17000, 64
     best = worst_splits(Mmax, K, Gmax, team_max, max_lt, C)
-    Ms = [0, 1, 80, 81, 113, 161, 225, 321, 449, 640, 641, 897, 1281, 4096, 6000, 16640, 17000]
+    Ms = [0, 1, 20, 21, 29, 41, 57, 80, 81, 113, 161, 225, 321, 449, 640, 641, 897, 1281, 4096, 6000,
+          16640, 17000]
     Gs = [1, 2, 4, 16, 64]
     triples = [(M, K, G, team_max, max_lt, C) for M in Ms for G in Gs]
     got = bound_tool(triples)
@@ -133,15 +138,17 @@ def test_bound_with_narrowed_strips(bound_tool, K, max_lt, C):
 
 def test_strip_cap_policy(bound_tool):
     """Tiny problems get strips narrow enough for one tile per CU (256 CUs);
-    every other shape keeps the widest strips the group sizes call for, and
-    K alone still caps the width."""
-    cases = [((4096, 4096, 16), 7), ((256, 4096, 4), 3), ((1024, 2048, 4), 3), ((16640, 8192, 64), 7),
-             ((65536, 4096, 8), 7), ((16640, 8192, 1), 7), ((81920, 8192, 16), 7),
-             ((4096, 64, 16), 3), ((2048, 8192, 64), 7), ((512, 4096, 8), 4)]
-    for C in CHUNKS:
+    every other shape keeps the widest strips the group sizes call for (up
+    to 4096 columns in the dim0 kernel, 1024 in the transposed one), and K
+    alone still caps the width. Expected caps: (dim0, dim0_t)."""
+    cases = [((4096, 4096, 16), (9, 7)), ((256, 4096, 4), (3, 3)), ((1024, 2048, 4), (3, 3)),
+             ((16640, 8192, 64), (9, 7)), ((65536, 4096, 8), (9, 7)), ((16640, 8192, 1), (9, 7)),
+             ((81920, 8192, 16), (9, 7)), ((4096, 64, 16), (3, 3)), ((2048, 8192, 64), (9, 7)),
+             ((512, 4096, 8), (4, 4)), ((16384, 2048, 512), (8, 7)), ((1024, 1024, 4), (3, 3))]
+    for ci, C in enumerate(CHUNKS):
         got = bound_tool([(M, K, G, 128, -256, C) for (M, K, G), _ in cases])
         for ((M, K, G), want), (lt,) in zip(cases, got):
-            assert lt == want, (M, K, G, C, lt, want)
+            assert lt == want[ci], (M, K, G, C, lt, want)
             # what the rule promises: a tile per CU for equal groups, unless the
             # narrowest strips are reached
             assert lt == 3 or G * tiles(M // G, K, 128, lt, C) >= 256
@@ -149,8 +156,8 @@ def test_strip_cap_policy(bound_tool):
 
 @pytest.mark.parametrize("C", CHUNKS)
 def test_bound_of_the_benchmark_shape(bound_tool, C):
-    (b, chunks, _), = bound_tool([(16640, 8192, 64, 128, 7, C)])
-    exact = int(worst_splits(16640, 8192, 64, 128, 7, C)[64][16640])
+    (b, chunks, _), = bound_tool([(16640, 8192, 64, 128, WIDEST[C], C)])
+    exact = int(worst_splits(16640, 8192, 64, 128, WIDEST[C], C)[64][16640])
     assert exact <= b
     assert chunks == 16640 // C + 16640 // (C + 1)
 

@@ -65,10 +65,12 @@ def data(seed, M, K):
 TEAM_MAX = [None, 1]      # the library's limit, then every tall group through maxima tiles
 
 
-# The first row count of each tiling step has the most tiles per row: 113 rows
-# (512-column strips), 225 (256), 449 (128), then 896 * (c - 1) + 1 rows for a
-# group cut into c chunks (897: two); the transposed kernel's steps (81, 161,
-# 321, 641, ...) are covered too. K values leave a ragged last strip.
+# The first row count of each tiling step has the most tiles per row: 29 rows
+# (2048-column strips), 57 (1024), 113 (512), 225 (256), 449 (128), then
+# 896 * (c - 1) + 1 rows for a group cut into c chunks (897: two); the
+# transposed kernel's steps (81, 161, 321, 641, ...) are covered too. K values
+# leave a ragged last strip, and the launches make at least one tile per CU,
+# so their strips are not narrowed.
 @pytest.mark.parametrize("team_max", TEAM_MAX)
 @pytest.mark.parametrize("size,n,K", [
     (113, 12, 2056), (225, 12, 1032), (449, 8, 520), (897, 6, 264), (1793, 3, 264),
@@ -76,6 +78,7 @@ TEAM_MAX = [None, 1]      # the library's limit, then every tall group through m
     (81, 12, 2056), (161, 12, 1032), (321, 10, 520), (641, 8, 264), (1281, 4, 264),
     (1921, 3, 136), (5121, 2, 264), (5121, 3, 72), (37, 16, 4104), (577, 4, 264),
     (865, 3, 136), (640, 5, 264), (1280, 3, 136),
+    (29, 100, 8200), (57, 60, 4104), (28, 90, 8200), (1, 300, 8200),
 ])
 def test_most_tiles_per_row(size, n, K, team_max):
     off = (np.arange(1, n + 1) * size).astype(np.int32)
@@ -84,10 +87,13 @@ def test_most_tiles_per_row(size, n, K, team_max):
 
 
 # Tiles whose rows run past the 20 register slabs into the LDS slabs, for
-# every strip width: rows 20 * rps .. 28 * rps - 1 (rps = 4, 8, 16, 32 rows
-# per slab), with ragged last slabs, ragged K and empty groups beside them.
+# every strip width: rows 20 * rps .. 28 * rps - 1 (rps = 1, 2, 4, 8, 16, 32
+# rows per slab), with ragged last slabs, ragged K and empty groups beside
+# them (the widest strips need enough tiles for one per CU).
 @pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("K,sizes", [
+    (8200, [28] * 90 + [20, 27, 0, 5]),    # 4096-column strips, rps = 1
+    (4104, [56] * 100 + [40, 55, 1]),      # 2048, rps = 2
     (2056, [81, 100, 0, 112, 7]),          # 1024-column strips, rps = 4
     (1032, [161, 200, 224, 3]),            # 512, rps = 8
     (520, [321, 400, 448, 16]),            # 256, rps = 16
