@@ -880,14 +880,15 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
     const int64_t per = n_tiles < (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid)
                             ? n_tiles : (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid);
     int64_t grid = xcd_split ? 8 * per : per;
-    // One to three rounds of tiles (by the bound): one resident round of
-    // workgroups instead, each walking its tiles b, b + grid, ... with no
-    // exit, dispatch and start between them. With more rounds, one
-    // workgroup per tile lets the hardware dispatcher balance tiles of
-    // unequal size; a fixed share of them was slower there. Teams stay
-    // consecutive in the tile order and hold fewer tiles than the grid, so
-    // the lowest tile in progress always has every teammate started or done.
-    if (!transposed && !xcd_split) {
+    // One group in one to three rounds of tiles (by the bound): one resident
+    // round of workgroups instead, each walking its tiles b, b + grid, ...
+    // with no exit, dispatch and start between them. Other launches keep one
+    // workgroup per tile, which lets the hardware dispatcher balance tiles:
+    // a fixed share of them was slower for groups of unequal size and for
+    // equal experts alike. Teams stay consecutive in the tile order and hold
+    // fewer tiles than the grid, so the lowest tile in progress always has
+    // every teammate started or done.
+    if (!transposed && !xcd_split && G == 1) {
         const int resident = dim0_resident(cus);
         if (resident > 0 && grid > resident && grid <= 3 * (int64_t)resident) grid = resident;
     }

@@ -9,8 +9,8 @@ that computes those maxima from x in the waiting tile itself (forced from
 the host by a negative wait bound), back-to-back calls on one stream and on
 two, the library's own workspace and caller-owned ones (which every call
 leaves zero-filled), replays of captured graphs, teams beside other
-kernels, and launches of a few rounds of tiles, which run as one resident
-round of workgroups."""
+kernels, and one-group launches of a few rounds of tiles, which run as one
+resident round of workgroups."""
 import numpy as np
 import pytest
 import torch
@@ -136,17 +136,19 @@ def test_tall_groups_without_the_wait(M, K, sizes, team_max):
     check(x, off, "zero wait %s" % (sizes,), team_max=team_max, spin=0)
 
 
-# Launches of one to three rounds of tiles (by the grid bound; (16640, 4096)
-# gives 608 to 1478 here) run as one resident round of workgroups, each
-# walking its tiles. At G=1 a 19-chunk team straddles the first round
-# (tiles 494-512); with a team limit of 4 the column-maximum tiles come
-# first and the casting tiles wait for maxima written in the same or an
-# earlier pass of the resident workgroups.
+# One group in one to three rounds of tiles (by the grid bound) runs as one
+# resident round of workgroups, each walking its tiles: (16640, 4096) gives
+# 608 tiles (1216 with a team limit of 4), and (30000, 2048) 544. A 19-chunk
+# team straddles the first round (tiles 494-512); with a team limit of 4
+# the column-maximum tiles come first and the casting tiles wait for maxima
+# written in the same or an earlier pass of the resident workgroups. Two
+# and three groups take the usual one workgroup per tile.
 @pytest.mark.parametrize("team_max", [None, 4])
-@pytest.mark.parametrize("sizes", [[16640], [6000, 10640], [0, 9000, 7640]])
-def test_resident_grid_launches(sizes, team_max):
+@pytest.mark.parametrize("M,K,sizes", [(16640, 4096, [16640]), (30000, 2048, [30000]),
+                                       (16640, 4096, [6000, 10640]), (16640, 4096, [0, 9000, 7640])])
+def test_resident_grid_launches(M, K, sizes, team_max):
     off = np.cumsum(sizes).astype(np.int32)
-    x = data(len(sizes) + 77, 16640, 4096)
+    x = data(len(sizes) + M // 1000, M, K)
     check(x, off, "resident grid %s" % (sizes,), team_max=team_max)
 
 
