@@ -340,6 +340,129 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
     return t;
 }
 
+// Words of the LDS scratch of find_tile_wide: block maxima, block totals
+// (column-maximum tiles, own tiles, chunk rows), the found flag and the tile.
+constexpr int kWaves = kThreads / kWave;
+constexpr int kSearchMax = 0;
+constexpr int kSearchTot = kWaves;
+constexpr int kSearchFlag = 4 * kWaves;
+constexpr int kSearchTile = 4 * kWaves + 1;
+constexpr int kSearchWords = kSearchTile + 12;
+
+// find_tile for launches of more than 64 groups (at most 1024): the
+// workgroup's 8 waves take 8 contiguous blocks of 64 or 128 groups and scan
+// them at once, then combine the blocks' maxima of the group ends and their
+// tile and chunk totals through LDS (three barriers); the wave that holds
+// the target publishes its tile. Same order, same tiles as find_tile; run by
+// every wave, and every lane returns the same tile.
+template <int kRows, bool kScalar>
+__device__ Tile find_tile_wide(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
+                               int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target,
+                               int* sx) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    // groups per wave: 64 up to 512 groups, else 128
+    const int np = G > kWaves * kWave ? 2 : 1;
+    const int b0 = w * np * kWave;
+    // ends, block by block: the running max inside this wave's block
+    int end[2], start[2];
+    int carry = 0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        end[p] = 0;
+        const int base = b0 + p * kWave;
+        if (p < np && base < G) {
+            const int raw = min(max(group_end_raw<kScalar>(off, base, G, M, uniform_rows), 0), M) & -row_align;
+            end[p] = max((int)wave_prefix_max((uint32_t)raw), carry);
+            carry = __builtin_amdgcn_readlane(end[p], kWave - 1);
+        }
+    }
+    if (lane == 0) {
+        sx[kSearchMax + w] = carry;
+        if (w == 0) sx[kSearchFlag] = 0;
+    }
+    __syncthreads();
+    int carry_end = 0;
+    for (int v = 0; v < w; ++v) carry_end = max(carry_end, sx[kSearchMax + v]);
+    // group rules and the block's prefix sums, from the global running max
+    GroupInfo gi[2];
+    int incl_x[2], incl_m[2], incl_ch[2];
+    int cx = 0, cm = 0, cch = 0;
+    int prev_end = carry_end;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int base = b0 + p * kWave;
+        const int e = max(end[p], carry_end);
+        start[p] = __builtin_amdgcn_update_dpp(prev_end, e, 0x138, 0xF, 0xF, false);
+        gi[p] = group_info<kRows>(start[p], e, p < np && base + lane < G, K, team_max, lt_cap);
+        incl_x[p] = maybe_c ? wave_prefix_sum_dpp(gi[p].cnt_x) + cx : 0;
+        incl_m[p] = wave_prefix_sum_dpp(gi[p].cnt_m) + cm;
+        incl_ch[p] = wave_prefix_sum_dpp(gi[p].chunks) + cch;
+        prev_end = __builtin_amdgcn_readlane(e, kWave - 1);
+        cx = __builtin_amdgcn_readlane(incl_x[p], kWave - 1);
+        cm = __builtin_amdgcn_readlane(incl_m[p], kWave - 1);
+        cch = __builtin_amdgcn_readlane(incl_ch[p], kWave - 1);
+    }
+    if (lane == 0) {
+        sx[kSearchTot + 3 * w] = cx;
+        sx[kSearchTot + 3 * w + 1] = cm;
+        sx[kSearchTot + 3 * w + 2] = cch;
+    }
+    __syncthreads();
+    int base_x = 0, base_m = 0, base_ch = 0, total_x = 0;
+    for (int v = 0; v < kWaves; ++v) {
+        const int tx = sx[kSearchTot + 3 * v];
+        total_x += tx;
+        if (v < w) {
+            base_x += tx;
+            base_m += sx[kSearchTot + 3 * v + 1];
+            base_ch += sx[kSearchTot + 3 * v + 2];
+        }
+    }
+    // column-maximum tiles come first; own tiles are numbered after them
+    const bool maxima = maybe_c && target < total_x;
+    const int tgt = maxima ? target : target - total_x;
+    Tile t;
+    t.g = -1;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int cnt = maxima ? gi[p].cnt_x : gi[p].cnt_m;
+        const int incl = (maxima ? base_x + incl_x[p] : base_m + incl_m[p]);
+        const uint64_t h = __ballot(p < np && cnt > 0 && tgt >= incl - cnt && tgt < incl);
+        if (h && t.g < 0) {
+            const int src = __ffsll((unsigned long long)h) - 1;
+            const int local = tgt - (__builtin_amdgcn_readlane(incl, src) - __builtin_amdgcn_readlane(cnt, src));
+            take_tile(t, gi[p], base_ch + incl_ch[p], src, b0 + p * kWave + src, local, maxima ? 1 : 0,
+                      row_align);
+        }
+    }
+    if (t.g >= 0 && lane == 0) {
+        int* d = sx + kSearchTile;
+        d[0] = t.g;  d[1] = t.maxima;  d[2] = t.cls;  d[3] = t.lt;  d[4] = t.strip;  d[5] = t.c;
+        d[6] = t.nc; d[7] = t.r0;      d[8] = t.r1;   d[9] = t.g0;  d[10] = t.g1;    d[11] = t.cbase;
+        sx[kSearchFlag] = 1;
+    }
+    __syncthreads();
+    Tile r;
+    r.g = -1;
+    if (__builtin_amdgcn_readfirstlane(sx[kSearchFlag])) {
+        const int* d = sx + kSearchTile;
+        r.g = __builtin_amdgcn_readfirstlane(d[0]);
+        r.maxima = __builtin_amdgcn_readfirstlane(d[1]);
+        r.cls = __builtin_amdgcn_readfirstlane(d[2]);
+        r.lt = __builtin_amdgcn_readfirstlane(d[3]);
+        r.strip = __builtin_amdgcn_readfirstlane(d[4]);
+        r.c = __builtin_amdgcn_readfirstlane(d[5]);
+        r.nc = __builtin_amdgcn_readfirstlane(d[6]);
+        r.r0 = __builtin_amdgcn_readfirstlane(d[7]);
+        r.r1 = __builtin_amdgcn_readfirstlane(d[8]);
+        r.g0 = __builtin_amdgcn_readfirstlane(d[9]);
+        r.g1 = __builtin_amdgcn_readfirstlane(d[10]);
+        r.cbase = __builtin_amdgcn_readfirstlane(d[11]);
+    }
+    return r;
+}
+
 // The lane number, computed where it is used: the compiler cannot hoist it,
 // so addresses derived from it do not stay live (and spill) across the
 // whole kernel.
@@ -586,7 +709,8 @@ __device__ __forceinline__ void dim0_body(
         const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ off, int G,
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
-        long long spin_ticks, int uniform_rows, int xcd_split, uint4* red, uint32_t* stage, uint4* ext) {
+        long long spin_ticks, int uniform_rows, int xcd_split, uint4* red, uint32_t* stage, uint4* ext,
+        int* search) {
     constexpr int kRowAlign = kT ? 16 : 1;
     constexpr int kRows = rows_w128<kT>();
     constexpr int kSlabs = reg_slabs<kT>();
@@ -604,8 +728,11 @@ __device__ __forceinline__ void dim0_body(
     // n_tiles < 2^31 and gridDim.x <= 2^22, so the unsigned sum never wraps
     for (unsigned item = first; item < (unsigned)n_tiles; item += stride) {
         MGS_TRACE_STAMP(tr0);
-        Tile t = find_tile<kRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign, uniform_rows,
-                                       (int)item);
+        Tile t = G > kWave
+                     ? find_tile_wide<kRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
+                                                  uniform_rows, (int)item, search)
+                     : find_tile<kRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
+                                             uniform_rows, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         t.strip += xcol * (Ks >> (t.lt + 3));
         const TileGeom geo = tile_geom(t, K);
@@ -822,8 +949,9 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
         long long spin_ticks, int uniform_rows, int xcd_split) {
     __shared__ uint4 red[kThreads];
     __shared__ uint4 ext[kLdsSlabs * kThreads];     // 64 KiB: the tile's rows past the registers
+    __shared__ int search[kSearchWords];
     dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
-                     ws_max, spin_ticks, uniform_rows, xcd_split, red, nullptr, ext);
+                     ws_max, spin_ticks, uniform_rows, xcd_split, red, nullptr, ext, search);
 }
 
 // The same per-group scaling with transposed outputs: qT (K, M), scalesT (K, G).
@@ -834,9 +962,10 @@ __global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
         long long spin_ticks, int uniform_rows, int xcd_split) {
     __shared__ uint4 red[kThreads];
     __shared__ uint4 stage[kStageWords / 4];
+    __shared__ int search[kSearchWords];
     dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
                     ws_max, spin_ticks, uniform_rows, xcd_split, red, reinterpret_cast<uint32_t*>(stage),
-                    nullptr);
+                    nullptr, search);
 }
 
 // Zero fill of n 16-byte words (a fresh workspace; no memset node, so the

@@ -26,9 +26,10 @@ untimed launches.
     python -m group_scaling_fp8_amd.tile_trace [--workload NAME ...] [--out FILE]
 
 Workloads: g64 and g1 (16640 x 8192 bf16; 64 groups at sorted uniform
-random cut points, multiples of 16 rows / one group), c2 (4096 x 4096, 16
-groups at random cut points, one of them empty and one all zero, pow2
-scales), c3 (65536 x 4096, 8 Dirichlet(0.5) groups).
+random cut points, multiples of 16 rows / one group), g256 and g1024 (the
+first 16640 / 16384 rows of the same tensor in 256 groups of 65 rows / 1024
+of 16), c2 (4096 x 4096, 16 groups at random cut points, one of them empty
+and one all zero, pow2 scales), c3 (65536 x 4096, 8 Dirichlet(0.5) groups).
 """
 from __future__ import annotations
 
@@ -72,6 +73,12 @@ def _workload(name):
         off = wl.target_offsets(64) if name == "g64" else np.array([T.shape[0]], np.int32)
         return ("(16640, 8192) bf16, %s" % ("64 groups at random cut points (0 to 1136 rows)"
                                              if name == "g64" else "one group"), T, off, False)
+    if name in ("g256", "g1024"):
+        T = wl.token_major_gradient()
+        n, rows = (256, 65) if name == "g256" else (1024, 16)
+        x = T[:n * rows]
+        return ("(%d, 8192) bf16, %d equal groups of %d rows" % (n * rows, n, rows), x,
+                (np.arange(1, n + 1) * rows).astype(np.int32), False)
     if name == "c2":
         w = wl.c2_dim0_pow2()
         return "(4096, 4096) bf16, 16 groups at random cut points, pow2 scales", w.x, w.offsets, True
@@ -330,7 +337,7 @@ def run(names, out_path=None):
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--workload", action="append", choices=("g64", "g1", "c2", "c3"))
+    ap.add_argument("--workload", action="append", choices=("g64", "g1", "g256", "g1024", "c2", "c3"))
     ap.add_argument("--out", default=None)
     args = ap.parse_args(argv)
     print(run(args.workload or ["g64", "c2"], args.out))

@@ -1,7 +1,7 @@
 """Seeded random shapes and group layouts for every entry point, each
 compared with the oracle byte for byte: arbitrary dim0 group boundaries
 (empty groups, groups of one row, groups cut into chunk teams, and with a
-team limit of 1 the column-maximum tiles), ragged K, both scale modes and
+team limit of 1 the column-maximum tiles; up to 1024 groups), ragged K, both scale modes and
 both MX modes, the transposed forms, the expert weights and the MX
 dequantisation of arbitrary code and scale bytes. Values mix normal draws
 with zeros of both signs, subnormals, the largest bf16 magnitudes and
@@ -72,6 +72,54 @@ def test_dim0_random(i):
     rq, rs = oracle.quant_groups_dim0(x, off, pow2)
     assert_same_bytes(s.cpu().numpy(), rs, "dim0 random %d scales" % i)
     assert_same_bytes(q.cpu().numpy(), rq, "dim0 random %d q" % i)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_dim0_many_groups_random(i):
+    """More than 64 groups: the tile search splits the groups over the
+    workgroup's waves. Up to the 1024-group limit, with runs of empty groups,
+    one-row groups, tall groups cut into teams and, with a team limit of 1
+    or 2, column-maximum tiles."""
+    rng = np.random.default_rng(12000 + i)
+    G = int(rng.choice([65, int(rng.integers(66, 512)), 512, 513, int(rng.integers(514, 1024)), 1024]))
+    M = int(rng.choice([int(rng.integers(1, 2000)), int(rng.integers(2000, 24000))]))
+    K = 8 * int(rng.integers(1, 200))
+    pow2 = bool(rng.random() < 0.5)
+    team_max = int(rng.choice([0, 0, 1, 2]))
+    print("dim0 many groups M=%d K=%d G=%d pow2=%d team_max=%d" % (M, K, G, pow2, team_max), flush=True)
+    x = values(rng, (M, K))
+    off = end_offsets(rng, M, G, 1)
+    if rng.random() < 0.3:
+        off[rng.integers(0, G):] = M            # the tail of the groups empty
+        off[-1] = M
+    xd, od = to_dev(x), to_dev(off)
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((G, K), dtype=torch.float32, device="cuda")
+    if team_max:
+        api._test_quant_dim0(xd, od, q, s, pow2=pow2, team_max=team_max)
+    else:
+        mgs.mgs_quant_groups_dim0(xd, od, pow2, q=q, scales=s)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_groups_dim0(x, off, pow2)
+    assert_same_bytes(s.cpu().numpy(), rs, "dim0 many groups %d scales" % i)
+    assert_same_bytes(q.cpu().numpy(), rq, "dim0 many groups %d q" % i)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_dim0_t_many_groups_random(i):
+    rng = np.random.default_rng(13000 + i)
+    G = int(rng.choice([65, int(rng.integers(66, 1024)), 1024]))
+    M = 16 * int(rng.integers(1, 1200))
+    K = 8 * int(rng.integers(1, 120))
+    pow2 = bool(rng.random() < 0.5)
+    print("dim0_t many groups M=%d K=%d G=%d pow2=%d" % (M, K, G, pow2), flush=True)
+    x = values(rng, (M, K))
+    off = end_offsets(rng, M, G, 16)
+    q_t, s_t = mgs.mgs_quant_groups_dim0_t(to_dev(x), to_dev(off), pow2)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_groups_dim0_t(x, off, pow2)
+    assert_same_bytes(s_t.cpu().numpy(), rs, "dim0_t many groups %d scales" % i)
+    assert_same_bytes(q_t.cpu().numpy(), rq, "dim0_t many groups %d q" % i)
 
 
 @pytest.mark.parametrize("i", range(12))
