@@ -77,7 +77,8 @@ namespace mgs {
 #if defined(MGS_TILE_TRACE)
 // Tile timeline, in trace builds only (libmgs_trace.so). For each tile item
 // i < kTraceTiles that casts (column-maximum tiles of class C are not
-// recorded), eight 64-bit words: five s_memrealtime stamps (100 MHz) at the
+// recorded; with the transposed kernel's XCD split, record 8 i + x holds
+// item i of XCD x), eight 64-bit words: five s_memrealtime stamps (100 MHz) at the
 // item's start, the tile found, its loads and column maxima done (a team
 // tile: after the team's maxima came in; a class C casting tile: after its
 // strip's maxima came in and its loads), the reduction across the workgroup
@@ -912,12 +913,15 @@ __device__ __forceinline__ void dim0_body(
             }
         }
 #if defined(MGS_TILE_TRACE)
-        if (threadIdx.x == 0 && item < (unsigned)kTraceTiles) {
+        // with the XCD split every XCD numbers its own tiles: record i holds
+        // tile item i / 8 of XCD i % 8
+        const unsigned rec = xcd_split ? item * 8u + (unsigned)xcol : item;
+        if (threadIdx.x == 0 && rec < (unsigned)kTraceTiles) {
             MGS_TRACE_STAMP(tr4);
             unsigned hw, xcc;
             asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
             asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-            unsigned long long* d = g_tile_trace + 8 * (size_t)item;
+            unsigned long long* d = g_tile_trace + 8 * (size_t)rec;
             d[0] = tr0;
             d[1] = tr1;
             d[2] = tr2;

@@ -3,7 +3,7 @@
 A diagnostic, not part of the quantisation path. It loads libmgs_trace.so
 (the same sources as libmgs.so built with MGS_TILE_TRACE, see build.py and
 include/mgs_trace.h) in place of libmgs.so, runs one dim0 workload through
-the ordinary entry point, reads back the per-tile stamps and prints a
+the ordinary entry point (or, with --transposed, dim0_t's), reads back the per-tile stamps and prints a
 markdown summary:
 
 - phases of a tile (search, loads and column maxima, reduction, cast and
@@ -23,7 +23,7 @@ run between one-thread stamp kernels, which give its start and end on the
 clock of the tile stamps. The GPU's clocks are settled first by 50 ms of
 untimed launches.
 
-    python -m group_scaling_fp8_amd.tile_trace [--workload NAME ...] [--out FILE]
+    python -m group_scaling_fp8_amd.tile_trace [--workload NAME ...] [--transposed] [--out FILE]
 
 Workloads: g64 and g1 (16640 x 8192 bf16; 64 groups at sorted uniform
 random cut points, multiples of 16 rows / one group), g256 and g1024 (the
@@ -205,7 +205,7 @@ def summarise(d: dict, kernel_us: float, edges=None) -> list:
     return out
 
 
-def run(names, out_path=None):
+def run(names, out_path=None, transposed=False):
     import torch
     L = _trace_library()
     from . import api as mgs
@@ -247,9 +247,10 @@ def run(names, out_path=None):
         sv = stamps.cpu().numpy()
         gaps.append((sv[1] - sv[0]) * TICK_US)
     props = torch.cuda.get_device_properties(0)
-    lines = ["# dim0 tile timeline", "",
-             "Command: `python -m group_scaling_fp8_amd.tile_trace %s%s` (%s, %s, %d compute units)." % (
-                 " ".join("--workload %s" % n for n in names), " --out FILE" if out_path else "",
+    lines = ["# dim0%s tile timeline" % ("_t" if transposed else ""), "",
+             "Command: `python -m group_scaling_fp8_amd.tile_trace %s%s%s` (%s, %s, %d compute units)." % (
+                 " ".join("--workload %s" % n for n in names), " --transposed" if transposed else "",
+                 " --out FILE" if out_path else "",
                  props.name, getattr(props, "gcnArchName", "?"), props.multi_processor_count), "",
              "The trace build runs the product kernel plus a few stores per tile, so its launches "
              "take a few us longer than libmgs.so's. Times are in us from the launch's first tile "
@@ -265,13 +266,23 @@ def run(names, out_path=None):
         off = torch.from_numpy(np.asarray(off_np, np.int32)).to(dev)
         M, K = x.shape
         ws = mgs.dim0_workspace(M, K)
-        q, s = mgs.mgs_quant_groups_dim0(x, off, pow2, workspace=ws)
+        if transposed:
+            q, s = mgs.mgs_quant_groups_dim0_t(x, off, pow2, workspace=ws)
+
+            def call(xx):
+                mgs.mgs_quant_groups_dim0_t(xx, off, pow2, q_t=q, scales_t=s, workspace=ws)
+        else:
+            q, s = mgs.mgs_quant_groups_dim0(x, off, pow2, workspace=ws)
+
+            def call(xx):
+                mgs.mgs_quant_groups_dim0(xx, off, pow2, q=q, scales=s, workspace=ws)
         t_pre = time.perf_counter()
         while (time.perf_counter() - t_pre) * 1e3 < PREWARM_MS:
-            mgs.mgs_quant_groups_dim0(x2, off, pow2, q=q, scales=s, workspace=ws)
+            call(x2)
         torch.cuda.synchronize()
+
         def launch(i):
-            mgs.mgs_quant_groups_dim0(x if i % 2 == 0 else x2, off, pow2, q=q, scales=s, workspace=ws)
+            call(x if i % 2 == 0 else x2)
 
         def time_b2b():
             """Per-launch time of three launches back to back, from stamp
@@ -322,8 +333,9 @@ def run(names, out_path=None):
             sv = stamps.cpu().numpy().astype(np.int64)
             d = decode(raw)
             edges = ((d["first_tick"] - sv[0]) * TICK_US, (sv[1] - d["last_tick"]) * TICK_US)
-            lines += ["## %s: %s, %s" % (name, desc, "the last of four launches back to back" if mode == "b2b"
-                                          else "one launch after a 1 GiB read sweep"), ""]
+            lines += ["## %s%s: %s, %s" % (name, " (dim0_t)" if transposed else "", desc,
+                                            "the last of four launches back to back" if mode == "b2b"
+                                            else "one launch after a 1 GiB read sweep"), ""]
             lines += summarise(d, kernel_us, edges) + [""]
             print("traced %s %s" % (name, mode), file=sys.stderr, flush=True)
         del x, x2, q, s, ws
@@ -338,9 +350,11 @@ def run(names, out_path=None):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--workload", action="append", choices=("g64", "g1", "g256", "g1024", "c2", "c3"))
+    ap.add_argument("--transposed", action="store_true",
+                    help="the transposed kernel (mgs_quant_groups_dim0_t); offsets must be multiples of 16")
     ap.add_argument("--out", default=None)
     args = ap.parse_args(argv)
-    print(run(args.workload or ["g64", "c2"], args.out))
+    print(run(args.workload or ["g64", "c2"], args.out, args.transposed))
 
 
 if __name__ == "__main__":
