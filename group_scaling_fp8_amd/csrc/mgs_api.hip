@@ -221,21 +221,24 @@ int quant_groups_dim0(const void* x, int64_t M, int64_t K, const int32_t* offset
         if (knobs->spin_ticks >= -1) spin_ticks = knobs->spin_ticks;
     }
     const int64_t chunk_rows = transposed ? mgs::kDim0ChunkRowsT : mgs::kDim0ChunkRows;
-    int lt_cap = mgs::dim0_lt_cap(M, K, n_groups, team_max, dinfo.cus, chunk_rows);
+    const int64_t lt_rows = transposed ? mgs::kDim0LtRowsT : mgs::kDim0LtRows;
+    const int max_lt = transposed ? mgs::kDim0MaxLtT : mgs::kDim0MaxLt;
+    int lt_cap = mgs::dim0_lt_cap(M, K, n_groups, team_max, dinfo.cus, chunk_rows, lt_rows, max_lt);
     // the transposed kernel deals its tiles to XCDs by column range when the
     // strips allow it, so that the 128-byte lines of q_t that two groups share
     // are written from one L2 (with teams that fit one XCD)
     bool xcd_split = false;
     if (transposed) {
         const int team_xcd = team_max < dinfo.cus / 8 ? team_max : (dinfo.cus / 8 > 0 ? dinfo.cus / 8 : 1);
-        const int lt_xcd = mgs::dim0_lt_cap(M, K, n_groups, team_xcd, dinfo.cus, chunk_rows);
+        const int lt_xcd = mgs::dim0_lt_cap(M, K, n_groups, team_xcd, dinfo.cus, chunk_rows, lt_rows,
+                                            max_lt);
         if (mgs::dim0_xcd_split(K, lt_xcd, dinfo.cus)) {
             xcd_split = true;
             team_max = team_xcd;
             lt_cap = lt_xcd;
         }
     }
-    if (mgs::dim0_tile_bound(M, K, n_groups, team_max, lt_cap, chunk_rows) >= INT32_MAX)
+    if (mgs::dim0_tile_bound(M, K, n_groups, team_max, lt_cap, chunk_rows, lt_rows) >= INT32_MAX)
         return MGS_ERR_UNSUPPORTED;
     void* w = ws;
     if (layout.bytes == 0) {

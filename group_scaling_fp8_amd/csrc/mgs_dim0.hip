@@ -18,20 +18,21 @@
 // below at 0, so any offsets array gives in-range rows.
 //
 // A 512-thread workgroup holds up to kSlabs 16-byte vectors per thread in
-// registers (160 KiB of bf16) and, in the plain kernel, kLdsSlabs more in LDS
-// (64 KiB, loaded straight from global memory with global_load_lds), and
-// every byte of x is loaded once into them. One CU alone streams only a few
-// tens of GB/s, so HBM is full only while every CU has loads in flight;
-// holding 224 KiB per tile lets a group of up to 896 rows (C below; 640 in
-// the transposed kernel, whose LDS holds its output stage) be one tile and
-// gives 449-896-row groups strips of 256 and 128 columns instead of chunk
-// teams. A tile is rows of one group times a strip of 8 * tpr columns, tpr
-// lanes per row:
+// registers (160 KiB of bf16) and kLdsSlabs more in LDS (64 KiB, loaded
+// straight from global memory with global_load_lds), and every byte of x is
+// loaded once into them. One CU alone streams only a few tens of GB/s, so
+// HBM is full only while every CU has loads in flight; holding 224 KiB per
+// tile lets a group of up to 896 rows (C below) be one tile and gives
+// 449-896-row groups strips of 256 and 128 columns instead of chunk teams.
+// The transposed kernel reuses the same LDS as its output stage once the
+// rows held there are cast. A tile is rows of one group times a strip of
+// 8 * tpr columns, tpr lanes per row:
 //   * class A, R <= C rows: one tile per strip. tpr is the widest power of
 //     two in [16, 512] whose tile fits (short groups get strips up to 4096
 //     columns; up to 1024 in the transposed kernel, whose LDS stage holds
-//     strips of at most that width). Load -> column amax -> scale -> cast
-//     from registers -> store.
+//     strips of at most that width, and which picks widths as if tiles held
+//     only their 640 register rows: its tiles cost more the more rows they
+//     hold). Load -> column amax -> scale -> cast from registers -> store.
 //     No strip is narrower than 128 columns unless K is, or the launch would
 //     otherwise have fewer tiles than CUs (lt_cap, from dim0_lt_cap): rows of
 //     128 bytes stream far worse than rows of 256.
@@ -95,14 +96,14 @@ __device__ unsigned long long g_tile_trace[kTraceTiles * 8];
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kLdsSlabs = kDim0LdsSlabs;              // vectors per thread in LDS (dim0 only)
+constexpr int kLdsSlabs = kDim0LdsSlabs;              // vectors per thread in LDS
 // vectors per thread in registers
 template <bool kT>
 constexpr int reg_slabs() { return kT ? kDim0SlabsT : kDim0Slabs; }
 // Rows of a full 128-column tile (16 lanes per row, 32 rows per slab): the
 // chunk size, and 8x / 4x / 2x the rows of the 1024 / 512 / 256-column steps.
 template <bool kT>
-constexpr int rows_w128() { return kThreads * (reg_slabs<kT>() + (kT ? 0 : kLdsSlabs)) / 16; }
+constexpr int rows_w128() { return kThreads * (reg_slabs<kT>() + kLdsSlabs) / 16; }
 static_assert(rows_w128<false>() == kDim0ChunkRows, "dim0 chunk size mismatch");
 static_assert(rows_w128<true>() == kDim0ChunkRowsT, "dim0_t chunk size mismatch");
 static_assert(kDim0ChunkRows % 8 == 0 && kDim0ChunkRowsT % 8 == 0, "strip steps");
@@ -130,7 +131,10 @@ struct GroupInfo {
     int chunks;     // workspace rows (classes T, C)
 };
 
-template <int kRows>
+// Strip widths step at kLtRows / 2^k rows (the rows of a full 128-column
+// tile that the kernel likes best: all of them in dim0, the register rows in
+// the transposed kernel); groups of more than kRows rows are cut into chunks.
+template <int kRows, int kLtRows>
 __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, int K, int team_max,
                                                 int lt_cap) {
     GroupInfo gi;
@@ -143,8 +147,8 @@ __device__ __forceinline__ GroupInfo group_info(int start, int end, bool valid, 
         gi.nc = (R + kRows - 1) / kRows;
         gi.cls = gi.nc <= team_max ? kClassT : kClassC;
     } else {
-        gi.lt = R <= kRows / 32 ? 9 : (R <= kRows / 16 ? 8 : (R <= kRows / 8 ? 7 :
-                (R <= kRows / 4 ? 6 : (R <= kRows / 2 ? 5 : 4))));
+        gi.lt = R <= kLtRows / 32 ? 9 : (R <= kLtRows / 16 ? 8 : (R <= kLtRows / 8 ? 7 :
+                (R <= kLtRows / 4 ? 6 : (R <= kLtRows / 2 ? 5 : 4))));
         gi.cls = kClassA;
     }
     // no strip wider than needed to cover K
@@ -269,7 +273,7 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
 // by every wave of the workgroup; all lanes return the same tile.
 // Group ends come from off (uniform_rows < 0), or are (g + 1) * uniform_rows
 // (equal groups, e.g. the experts of a 3D weight, with no offsets array).
-template <int kRows, bool kScalar>
+template <int kRows, int kLtRows, bool kScalar>
 __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
                           int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -284,7 +288,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         // the previous lane's end (wave_shr:1); lane 0 keeps carry_end
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
-        const GroupInfo gi = group_info<kRows>(start, end, g < G, K, team_max, lt_cap);
+        const GroupInfo gi = group_info<kRows, kLtRows>(start, end, g < G, K, team_max, lt_cap);
         const int incl_x = maybe_c ? wave_prefix_sum_dpp(gi.cnt_x) + carry_x : 0;
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
@@ -323,7 +327,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
         const int raw = min(max(group_end_raw<kScalar>(off, base, G, M, uniform_rows), 0), M) & -row_align;
         const int end = max((int)wave_prefix_max((uint32_t)raw), carry_end);
         const int start = __builtin_amdgcn_update_dpp(carry_end, end, 0x138, 0xF, 0xF, false);
-        const GroupInfo gi = group_info<kRows>(start, end, g < G, K, team_max, lt_cap);
+        const GroupInfo gi = group_info<kRows, kLtRows>(start, end, g < G, K, team_max, lt_cap);
         const int incl_m = wave_prefix_sum_dpp(gi.cnt_m) + carry_m;
         const int incl_ch = wave_prefix_sum_dpp(gi.chunks) + carry_ch;
         const uint64_t hm = __ballot(gi.cnt_m > 0 && target >= incl_m - gi.cnt_m && target < incl_m);
@@ -356,7 +360,7 @@ constexpr int kSearchWords = kSearchTile + 12;
 // tile and chunk totals through LDS (three barriers); the wave that holds
 // the target publishes its tile. Same order, same tiles as find_tile; run by
 // every wave, and every lane returns the same tile.
-template <int kRows, bool kScalar>
+template <int kRows, int kLtRows, bool kScalar>
 __device__ Tile find_tile_wide(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
                                int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target,
                                int* sx) {
@@ -395,7 +399,7 @@ __device__ Tile find_tile_wide(const int32_t* __restrict__ off, int G, int M, in
         const int base = b0 + p * kWave;
         const int e = max(end[p], carry_end);
         start[p] = __builtin_amdgcn_update_dpp(prev_end, e, 0x138, 0xF, 0xF, false);
-        gi[p] = group_info<kRows>(start[p], e, p < np && base + lane < G, K, team_max, lt_cap);
+        gi[p] = group_info<kRows, kLtRows>(start[p], e, p < np && base + lane < G, K, team_max, lt_cap);
         incl_x[p] = maybe_c ? wave_prefix_sum_dpp(gi[p].cnt_x) + cx : 0;
         incl_m[p] = wave_prefix_sum_dpp(gi[p].cnt_m) + cm;
         incl_ch[p] = wave_prefix_sum_dpp(gi[p].chunks) + cch;
@@ -570,27 +574,32 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Plain layout only: slabs kSlabs .. kSlabs + kLdsSlabs - 1 (rows
-// (kSlabs + e) * rps + ty) go straight from global memory into LDS
-// (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the wave's
-// LDS base + 16 i), so thread t owns ext[e * kThreads + t]. Lanes whose row
-// or columns do not exist load nothing, and ext_slab masks them.
+// Slabs kSlabs .. kSlabs + kLdsSlabs - 1 (rows slab_row(kSlabs + e, rps,
+// ty)) go straight from global memory into LDS (global_load_lds_dwordx4:
+// lane i of a wave writes 16 bytes at the wave's LDS base + 16 i), so thread
+// t owns ext[e * kThreads + t]. Lanes whose row or columns do not exist load
+// nothing, and ext_slab masks them.
+template <bool kQuad>
 __device__ __forceinline__ void load_tile_ext(const uint16_t* __restrict__ x, int64_t K, int r0,
                                               int nrows, const TileGeom& q, uint4* ext) {
+    constexpr int kSlabs = reg_slabs<kQuad>();
     const int wave = threadIdx.x / kWave;
-    const uint16_t* p = x + (int64_t)(r0 + kDim0Slabs * q.rps + q.ty) * K + q.col;
+    const uint16_t* p = x + (int64_t)(r0 + slab_row<kQuad>(kSlabs, q.rps, q.ty)) * K + q.col;
 #pragma unroll
     for (int e = 0; e < kLdsSlabs; ++e) {
-        const int r_s = (kDim0Slabs + e) * q.rps;
-        if (r_s + q.ty < nrows && q.col_ok)
+        const int r = slab_row<kQuad>(kSlabs + e, q.rps, q.ty);
+        if (r < nrows && q.col_ok)
             __builtin_amdgcn_global_load_lds(p, (lds_void*)(ext + e * kThreads + wave * kWave), 16, 0,
                                              kLoadNontemporal);
-        p += (int64_t)q.rps * K;
+        if (e + 1 < kLdsSlabs)
+            p += (int64_t)(slab_row<kQuad>(kSlabs + e + 1, q.rps, 0) - slab_row<kQuad>(kSlabs + e, q.rps, 0)) * K;
     }
 }
 
+template <bool kQuad>
 __device__ __forceinline__ uint4 ext_slab(const uint4* ext, int e, int nrows, const TileGeom& q) {
-    if ((kDim0Slabs + e) * q.rps + q.ty < nrows && q.col_ok) return ext[e * kThreads + threadIdx.x];
+    if (slab_row<kQuad>(reg_slabs<kQuad>() + e, q.rps, q.ty) < nrows && q.col_ok)
+        return ext[e * kThreads + threadIdx.x];
     return make_uint4(0u, 0u, 0u, 0u);
 }
 
@@ -690,17 +699,46 @@ __device__ __forceinline__ bool gather_maxima(uint64_t* ws_max, const Tile& t, i
     return true;
 }
 
-// Staging of the transposed tile in LDS: per tile column a row of 4-byte
-// words (a multiple of 16 of them), each word holding four consecutive rows.
-// The word index is XOR-swizzled with the lane's column block (within its
-// 16-word block) so that the lanes of a wave spread over the banks. Three
-// quads of rows of any strip width fit: 8 << lt columns x 16 * 2^(7 - lt)
-// words at most 16384 words.
-constexpr int kStageWords = 16384;        // 64 KiB
-__device__ __forceinline__ int stage_pitch(int rps) {
-    return (3 * rps + 15) & ~15;          // words per column: three quads of rows
+// Staging of the transposed tile in LDS: per tile column a row of pw 4-byte
+// words (a power of two, at least 8), word u holding the four consecutive
+// rows row_a + 4u .. + 3. The 4-word group of a word index is XOR-swizzled
+// with the lane's column block within its aligned block of min(pw, 64)
+// words, so that the lanes of a wave writing one row quad spread over the
+// banks. The register rows pass in two phases with pw = 4 * rps (room for
+// four quads: 8 << lt columns x 4 * (512 >> lt) words, 16384 words at any
+// strip width); the two quads of the LDS rows pass before them with
+// pw = 2 * rps, in half of that.
+constexpr int kStageWords = kLdsSlabs * kThreads * 4;     // 64 KiB, the LDS rows' space
+static_assert(kStageWords == 16384, "stage size");
+static_assert(kLdsSlabs == 8 && reg_slabs<true>() == 20,
+              "the stage takes the LDS rows as quads 5..6, the register rows as quads 0..2 and 3..4");
+__device__ __forceinline__ int stage_pitch(int rps) { return 4 * rps; }
+__device__ __forceinline__ int stage_swizzle(int col_block, int pw) {
+    const int groups = (pw < 64 ? pw : 64) >> 2;
+    return (col_block & (groups - 1)) << 2;
 }
-__device__ __forceinline__ int stage_swizzle(int col_block) { return (col_block & 3) << 2; }
+
+// Stores rows [row_a, row_b) of the tile's ncols columns from the stage to
+// q_t (qstrip: the strip's first q_t row at the tile's first row) in pieces
+// of 16 rows of one column, consecutive lanes along the rows of a column:
+// c = p / npc by a multiply-shift, exact since p < ncols * npc <= 3072 and
+// npc <= 48.
+__device__ __forceinline__ void store_staged(const uint32_t* stage, int pw, int ncols, int row_a,
+                                             int row_b, uint8_t* qstrip, int64_t M) {
+    const int npc = (row_b - row_a) >> 4;
+    const uint32_t inv = ((1u << 20) + (uint32_t)npc - 1u) / (uint32_t)npc;
+    const int total = ncols * npc;
+    uint8_t* qbase = qstrip + row_a;
+    for (int p = threadIdx.x; p < total; p += kThreads) {
+        const int c = (int)(((uint32_t)p * inv) >> 20);
+        const int k = p - c * npc;
+        const uint4 val = *reinterpret_cast<const uint4*>(stage + c * pw + ((4 * k) ^ stage_swizzle(c >> 3, pw)));
+        // an ordinary store: a group's run of a q_t row starts on a 16-byte
+        // boundary only, and L2 merges the two tiles' parts of a shared line
+        // (nontemporal partial lines cost far more)
+        *reinterpret_cast<uint4*>(qbase + (int64_t)c * M + 16 * k) = val;
+    }
+}
 
 // One tile: load, column amax (across chunk tiles when the group is cut),
 // scales, cast. kT: q is (K, M) and scales (K, G), the transposes of dim0's
@@ -714,6 +752,7 @@ __device__ __forceinline__ void dim0_body(
         int* search) {
     constexpr int kRowAlign = kT ? 16 : 1;
     constexpr int kRows = rows_w128<kT>();
+    constexpr int kLtRows = kT ? kDim0LtRowsT : kDim0LtRows;
     constexpr int kSlabs = reg_slabs<kT>();
     const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x) < kWave;
 
@@ -730,9 +769,9 @@ __device__ __forceinline__ void dim0_body(
     for (unsigned item = first; item < (unsigned)n_tiles; item += stride) {
         MGS_TRACE_STAMP(tr0);
         Tile t = G > kWave
-                     ? find_tile_wide<kRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
+                     ? find_tile_wide<kRows, kLtRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
                                                   uniform_rows, (int)item, search)
-                     : find_tile<kRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
+                     : find_tile<kRows, kLtRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
                                              uniform_rows, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         t.strip += xcol * (Ks >> (t.lt + 3));
@@ -762,9 +801,9 @@ __device__ __forceinline__ void dim0_body(
 
         uint4 v[kSlabs];
         load_tile<kT>(x, K, t.r0, nrows, geo, v);
-        // rows past the registers' (plain layout): into LDS
-        const bool use_ext = !kT && kSlabs * geo.rps < nrows;
-        if (use_ext) load_tile_ext(x, K, t.r0, nrows, geo, ext);
+        // rows past the registers': into LDS
+        const bool use_ext = kSlabs * geo.rps < nrows;
+        if (use_ext) load_tile_ext<kT>(x, K, t.r0, nrows, geo, ext);
         if (t.cls != kClassC || t.maxima) {
 #pragma unroll
             for (int s = 0; s < kSlabs; ++s)
@@ -775,7 +814,7 @@ __device__ __forceinline__ void dim0_body(
             __builtin_amdgcn_s_waitcnt(0);
             if (t.cls != kClassC || t.maxima) {
 #pragma unroll
-                for (int e = 0; e < kLdsSlabs; ++e) max4(m, ext_slab(ext, e, nrows, geo));
+                for (int e = 0; e < kLdsSlabs; ++e) max4(m, ext_slab<kT>(ext, e, nrows, geo));
             }
         }
 
@@ -859,12 +898,53 @@ __device__ __forceinline__ void dim0_body(
                 dst[6 * (int64_t)G] = s6;
                 dst[7 * (int64_t)G] = s7;
             }
-            // Two phases through the stage: row quads 0..2, then 3..4. Tile
-            // rows and their starts are multiples of 16, so every quad is
-            // whole and every output piece is 16 aligned bytes.
-            const int pw = stage_pitch(geo.rps);
+            // Tile rows and their starts are multiples of 16, so every quad
+            // is whole and every output piece is 16 aligned bytes.
             const int W = geo.tpr * 8;
             const int ncols = min(W, K - t.strip * W);
+            uint8_t* qstrip = q + (int64_t)(t.strip * W) * M + t.r0;
+            if (use_ext) {
+                // The rows in LDS (quads 5 and 6) go first, so that all of the
+                // LDS is free for the stage afterwards. Cast in place: slot e
+                // of this thread (e < 4) takes the cast of its vectors e and
+                // e + 4, so the upper half of the LDS (vectors 4..7) is free
+                // once every thread has read its own.
+                uint2* own = reinterpret_cast<uint2*>(ext + threadIdx.x);
+#pragma unroll
+                for (int e = 0; e < kLdsSlabs; ++e) {
+                    const uint2 c = cast8_group(ext_slab<true>(ext, e, nrows, geo), s0, s1, s2, s3, s4, s5,
+                                                s6, s7);
+                    own[(e & 3) * 2 * kThreads + (e >> 2)] = c;
+                }
+                __syncthreads();
+                uint32_t* st = reinterpret_cast<uint32_t*>(ext + 4 * kThreads);   // 32 KiB
+                const int pw = 2 * geo.rps;           // two quads of rows per column
+                uint32_t* col_base = st + geo.tx * 8 * pw;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 4 * ((kSlabs / 4 + h) * geo.rps + geo.ty);
+                    if (row < nrows && geo.col_ok) {
+                        const uint2 b0 = own[0 * 2 * kThreads + h], b1 = own[1 * 2 * kThreads + h];
+                        const uint2 b2 = own[2 * 2 * kThreads + h], b3 = own[3 * 2 * kThreads + h];
+                        uint32_t lo[4], hi[4];
+                        transpose4x4(b0.x, b1.x, b2.x, b3.x, lo);
+                        transpose4x4(b0.y, b1.y, b2.y, b3.y, hi);
+                        const int w = (h * geo.rps + geo.ty) ^ stage_swizzle(geo.tx, pw);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            col_base[j * pw + w] = lo[j];
+                            col_base[(j + 4) * pw + w] = hi[j];
+                        }
+                    }
+                }
+                __syncthreads();
+                store_staged(st, pw, ncols, kSlabs * geo.rps,
+                             min(4 * (kSlabs / 4 + 2) * geo.rps, nrows), qstrip, M);
+                __syncthreads();      // the stage's reads are done
+            }
+            // The register rows in two phases through the stage: row quads
+            // 0..2, then 3..4.
+            const int pw = stage_pitch(geo.rps);
             for (int ph = 0; ph < 2; ++ph) {
                 const int qa = ph ? 3 : 0, qb = ph ? 5 : 3;
                 const int row_a = 4 * qa * geo.rps;
@@ -884,7 +964,7 @@ __device__ __forceinline__ void dim0_body(
                         uint32_t lo[4], hi[4];
                         transpose4x4(b0.x, b1.x, b2.x, b3.x, lo);
                         transpose4x4(b0.y, b1.y, b2.y, b3.y, hi);
-                        const int w = ((qd - qa) * geo.rps + geo.ty) ^ stage_swizzle(geo.tx);
+                        const int w = ((qd - qa) * geo.rps + geo.ty) ^ stage_swizzle(geo.tx, pw);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             col_base[j * pw + w] = lo[j];
@@ -893,23 +973,7 @@ __device__ __forceinline__ void dim0_body(
                     }
                 }
                 __syncthreads();
-                // pieces of 16 rows of one column, consecutive lanes along the
-                // rows of a column: c = p / npc by a multiply-shift, exact since
-                // p < ncols * npc <= 3072 and npc <= 48
-                const int npc = (row_b - row_a) >> 4;
-                const uint32_t inv = ((1u << 20) + (uint32_t)npc - 1u) / (uint32_t)npc;
-                const int total = ncols * npc;
-                uint8_t* qbase = q + (int64_t)(t.strip * W) * M + (t.r0 + row_a);
-                for (int p = threadIdx.x; p < total; p += kThreads) {
-                    const int c = (int)(((uint32_t)p * inv) >> 20);
-                    const int k = p - c * npc;
-                    const uint4 val = *reinterpret_cast<const uint4*>(
-                        stage + c * pw + ((4 * k) ^ stage_swizzle(c >> 3)));
-                    // an ordinary store: a group's run of a q_t row starts on a
-                    // 16-byte boundary only, and L2 merges the two tiles' parts
-                    // of a shared line (nontemporal partial lines cost far more)
-                    *reinterpret_cast<uint4*>(qbase + (int64_t)c * M + 16 * k) = val;
-                }
+                store_staged(stage, pw, ncols, row_a, row_b, qstrip, M);
             }
         }
 #if defined(MGS_TILE_TRACE)
@@ -965,11 +1029,11 @@ __global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
         int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
         long long spin_ticks, int uniform_rows, int xcd_split) {
     __shared__ uint4 red[kThreads];
-    __shared__ uint4 stage[kStageWords / 4];
+    __shared__ uint4 ext[kLdsSlabs * kThreads];     // 64 KiB: rows past the registers, then the stage
     __shared__ int search[kSearchWords];
     dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
-                    ws_max, spin_ticks, uniform_rows, xcd_split, red, reinterpret_cast<uint32_t*>(stage),
-                    nullptr, search);
+                    ws_max, spin_ticks, uniform_rows, xcd_split, red, reinterpret_cast<uint32_t*>(ext),
+                    ext, search);
 }
 
 // Zero fill of n 16-byte words (a fresh workspace; no memset node, so the
@@ -1007,8 +1071,10 @@ hipError_t launch_dim0(const uint16_t* x, int M, int K, const int32_t* off, int 
                        bool pow2, bool transposed, uint8_t* q, float* scales, int team_max, int lt_cap,
                        bool xcd_split, void* ws, long long spin_ticks, int cus, hipStream_t stream) {
     const int64_t chunk_rows = transposed ? kDim0ChunkRowsT : kDim0ChunkRows;
+    const int64_t lt_rows = transposed ? kDim0LtRowsT : kDim0LtRows;
     // with xcd_split every XCD runs the tiling of K / 8 columns
-    const int64_t n_tiles = dim0_tile_bound(M, xcd_split ? K / 8 : K, G, team_max, lt_cap, chunk_rows);
+    const int64_t n_tiles =
+        dim0_tile_bound(M, xcd_split ? K / 8 : K, G, team_max, lt_cap, chunk_rows, lt_rows);
     if (n_tiles >= INT32_MAX) return hipErrorInvalidValue;
     const int64_t per = n_tiles < (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid)
                             ? n_tiles : (xcd_split ? kDim0MaxGrid / 8 : kDim0MaxGrid);

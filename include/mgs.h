@@ -90,8 +90,8 @@ enum { MGS_MX_FLOOR = 0, MGS_MX_RCEIL = 1 };
  * 896 rows (a tile holds 896 rows of 128 columns: 160 KiB in registers and
  * 64 KiB in LDS). The chunks' column maxima pass between workgroups of the
  * one kernel launch through a device workspace of
- * mgs_dim0_workspace_bytes(M, K) bytes (0 when M <= 640, else about
- * M * K / 80 bytes). A tile that waits for other tiles' maxima waits at most
+ * mgs_dim0_workspace_bytes(M, K) bytes (0 when M <= 896, else about
+ * M * K / 112 bytes). A tile that waits for other tiles' maxima waits at most
  * about 20 ms of device wall clock; past that it computes them from x
  * itself, so the result never depends on workgroup scheduling.
  * Memory: this call takes no workspace argument (its signature is the one
@@ -115,8 +115,8 @@ int mgs_quant_groups_dim0(const void *x, int64_t M, int64_t K,
 /*
  * Size in bytes of the workspace that the dim0-family calls on an (M, K)
  * input need (mgs_quant_groups_dim0_ws, mgs_quant_groups_dim0_t, and
- * mgs_quant_experts_dim1 with M = E * D1, K = D2): 0 when M <= 640 (no group
- * can be cut into chunks), else, with c = M / 640 + M / 641 chunk rows,
+ * mgs_quant_experts_dim1 with M = E * D1, K = D2): 0 when M <= 896 (no group
+ * can be cut into chunks), else, with c = M / 896 + M / 897 chunk rows,
  * round_up(4 * c * ceil(K / 128), 256) + 8 * c * (K / 2).
  * Host only; no GPU work. Returns MGS_ERR_INVALID_ARG for a null `bytes` or
  * negative sizes, MGS_ERR_UNSUPPORTED for M or K over 2^31 - 1.
@@ -159,7 +159,7 @@ int mgs_quant_groups_dim0_ws(const void *x, int64_t M, int64_t K,
  * inside the library's code object, one per device, held until the process
  * ends. Arguments, results and errors are those of mgs_quant_groups_dim0,
  * plus MGS_ERR_UNSUPPORTED when mgs_dim0_workspace_bytes(M, K) exceeds that
- * size (roughly M * K > 1.3e9; inputs with M <= 640 need no workspace at
+ * size (roughly M * K > 1.8e9; inputs with M <= 896 need no workspace at
  * all). Allocates and frees nothing. The first call on a device that needs
  * the array clears it with a kernel queued on the call's stream (a call
  * captured before any eager one puts that clear into its graph); every call
@@ -194,10 +194,10 @@ int mgs_quant_groups_dim0_noalloc(const void *x, int64_t M, int64_t K,
  *            the library's own workspace).
  * Requirements: M % 16 == 0, K % 8 == 0; x and q_t 16-byte aligned,
  * scales_t 4-byte aligned. M == 0 writes only the scales; K == 0 is a
- * no-op. The bounded wait and errors are as for mgs_quant_groups_dim0_ws,
- * except that tiles hold 640 rows of 128 columns (all in registers: LDS
- * holds the transposed output stage), so groups taller than 640 rows are cut
- * into chunks of at most 640 rows.
+ * no-op. Tiles, chunks, the bounded wait and errors are as for
+ * mgs_quant_groups_dim0_ws (the LDS that holds a tile's last rows is reused
+ * as the transposed output stage once they are cast), except that strips
+ * are at most 1024 columns wide.
  */
 int mgs_quant_groups_dim0_t(const void *x, int64_t M, int64_t K,
                             const int32_t *offsets, int32_t n_groups,

@@ -110,7 +110,7 @@ def test_grouped_argument_errors(L, fn):
         assert call(M=2000, ws=A, wsb=need.value - 8) == INVALID
     if fn.endswith("_noalloc"):
         # inputs whose workspace would exceed the fixed scratch array
-        assert call(M=200000, K=8192) == UNSUPPORTED
+        assert call(M=300000, K=8192) == UNSUPPORTED
     if fn.endswith("dim0") or fn.endswith("dim0_ws") or fn.endswith("_noalloc"):
         assert call(K=12) == INVALID
         assert call(s=A + 4) == INVALID
@@ -148,12 +148,12 @@ def test_experts_argument_errors(L):
 
 def test_workspace_size_query(L):
     n = ctypes.c_int64(-1)
-    assert L.mgs_dim0_workspace_bytes(640, 4096, ctypes.byref(n)) == mgs.MGS_OK and n.value == 0
+    assert L.mgs_dim0_workspace_bytes(896, 4096, ctypes.byref(n)) == mgs.MGS_OK and n.value == 0
     def expect(M, K):
-        c = M // 640 + M // 641
+        c = M // 896 + M // 897
         return -(-4 * c * -(-K // 128) // 256) * 256 + 8 * c * (K // 2)
-    assert L.mgs_dim0_workspace_bytes(641, 8, ctypes.byref(n)) == mgs.MGS_OK
-    assert n.value == expect(641, 8) == 256 + 8 * 2 * 4
+    assert L.mgs_dim0_workspace_bytes(897, 8, ctypes.byref(n)) == mgs.MGS_OK
+    assert n.value == expect(897, 8) == 256 + 8 * 2 * 4
     assert L.mgs_dim0_workspace_bytes(16640, 8192, ctypes.byref(n)) == mgs.MGS_OK
     assert n.value == expect(16640, 8192)
     assert L.mgs_dim0_workspace_bytes(-1, 8, ctypes.byref(n)) == INVALID

@@ -4,12 +4,13 @@ The dim0 launch has one workgroup per tile and sizes its grid from (M, K, G)
 alone, so the bound must hold for every way of splitting M rows into G
 groups. The tile count of a group depends only on its row count, as a step
 function, so the worst split is found exactly by a knapsack over the first
-row count of each step (0, C/32 + 1, C/16 + 1, C/8 + 1, C/4 + 1, C/2 + 1,
-then C * (c - 1) + 1 for the groups cut into c >= 2 chunks, with C the chunk
-rows: 896 for the dim0 kernel, 640 for the transposed one). The C++ bound, compiled with g++
-from the header the library uses, must be at least that worst case, for
-several team limits (the most chunks a group may have to be cast as a
-team)."""
+row count of each step (0, L/32 + 1, L/16 + 1, L/8 + 1, L/4 + 1, L/2 + 1,
+then C * (c - 1) + 1 for the groups cut into c >= 2 chunks, with C = 896
+the chunk rows of both kernels and L the rows at which strip widths step:
+896 in the dim0 kernel, 640 in the transposed one, whose strips are also at
+most 1024 columns wide against 4096). The C++ bound, compiled with g++ from
+the header the library uses, must be at least that worst case, for several
+team limits (the most chunks a group may have to be cast as a team)."""
 import math
 import os
 import subprocess
@@ -25,35 +26,43 @@ BOUND_PROGRAM = r"""
 #include <stdio.h>
 #include "mgs_dim0_layout.hpp"
 int main() {
-    long long M, K, G, T, L, C;
-    while (scanf("%lld %lld %lld %lld %lld %lld", &M, &K, &G, &T, &L, &C) == 6) {
-        if (L < 0) {   // the strip-width cap for a device of -L compute units
-            printf("%d\n", mgs::dim0_lt_cap(M, K, G, T, -L, C));
+    long long M, K, G, T, L, C, LR, X;
+    while (scanf("%lld %lld %lld %lld %lld %lld %lld %lld", &M, &K, &G, &T, &L, &C, &LR, &X) == 8) {
+        if (L < 0) {   // the strip-width cap for a device of -L compute units, widest 8 << X
+            printf("%d\n", mgs::dim0_lt_cap(M, K, G, T, -L, C, LR, (int)X));
             continue;
         }
-        printf("%lld %lld %lld\n", (long long)mgs::dim0_tile_bound(M, K, G, T, (int)L, C),
+        printf("%lld %lld %lld\n", (long long)mgs::dim0_tile_bound(M, K, G, T, (int)L, C, LR),
                (long long)mgs::dim0_chunk_bound(M, C),
-               (long long)mgs::dim0_group_tiles(M, K, T, (int)L, C));
+               (long long)mgs::dim0_group_tiles(M, K, T, (int)L, C, LR));
     }
     return 0;
 }
 """
 
 
-CHUNKS = [896, 640]      # chunk rows of the dim0 and dim0_t kernels
-WIDEST = {896: 9, 640: 7}   # their widest strips: 4096 and 1024 columns
+C896 = 896
+# (chunk rows, rows at which strip widths step, widest strips) of the dim0
+# and dim0_t kernels: strips of at most 4096 and 1024 columns
+KERNELS = [(896, 896, 9), (896, 640, 7)]
 
 
-def tiles(R, K, team_max, max_lt=7, C=896):
+def group_lt(R, C=896, LR=None):
+    """Strip width of a group of R rows before any cap (the rule of the
+    kernel's tile search): strips of 8 << lt columns."""
+    LR = C if LR is None else LR
+    if R > LR // 2:
+        return 4
+    return (9 if R <= LR // 32 else 8 if R <= LR // 16 else 7 if R <= LR // 8 else
+            6 if R <= LR // 4 else 5)
+
+
+def tiles(R, K, team_max, max_lt=7, C=896, LR=None):
     """Tiles of one group of R rows (the rule of the kernel's tile search),
-    with strips at most 8 << max_lt columns wide and chunks of C rows."""
-    if R > C:
-        lt, chunks = 4, -(-R // C)
-    else:
-        lt = (9 if R <= C // 32 else 8 if R <= C // 16 else 7 if R <= C // 8 else
-              6 if R <= C // 4 else 5 if R <= C // 2 else 4)
-        chunks = 0
-    lt = min(lt, max_lt)
+    with strips at most 8 << max_lt columns wide, chunks of C rows and strip
+    widths stepping at LR / 2^k rows."""
+    chunks = -(-R // C) if R > C else 0
+    lt = min(group_lt(R, C, LR), max_lt)
     while lt > 3 and (8 << (lt - 1)) >= K:
         lt -= 1
     ns = -(-K // (8 << lt))
@@ -62,10 +71,11 @@ def tiles(R, K, team_max, max_lt=7, C=896):
     return (1 if chunks <= team_max else 2) * chunks * ns
 
 
-def worst_splits(Mmax, K, Gmax, team_max, max_lt=7, C=896):
+def worst_splits(Mmax, K, Gmax, team_max, max_lt=7, C=896, LR=None):
     """best[G][M] = the most tiles over all splits of at most M rows into
     exactly G groups."""
-    sizes = [0, C // 32 + 1, C // 16 + 1, C // 8 + 1, C // 4 + 1, C // 2 + 1] + \
+    LR = C if LR is None else LR
+    sizes = [0, LR // 32 + 1, LR // 16 + 1, LR // 8 + 1, LR // 4 + 1, LR // 2 + 1] + \
         [C * (c - 1) + 1 for c in range(2, Mmax // C + 3)]
     sizes = [r for r in sizes if r <= Mmax]
     NEG = -(1 << 40)
@@ -75,7 +85,7 @@ def worst_splits(Mmax, K, Gmax, team_max, max_lt=7, C=896):
     for _ in range(Gmax):
         nxt = np.full(Mmax + 1, NEG, np.int64)
         for r in sizes:
-            t = tiles(r, K, team_max, max_lt, C)
+            t = tiles(r, K, team_max, max_lt, C, LR)
             np.maximum(nxt[r:], dp[:Mmax + 1 - r] + t, out=nxt[r:])
         dp = nxt
         best.append(np.maximum.accumulate(dp))
@@ -92,48 +102,49 @@ def bound_tool():
     subprocess.run(["g++", "-O1", "-std=c++17", "-I", CSRC, "-o", exe, src], check=True)
 
     def run(triples):
-        inp = "".join("%d %d %d %d %d %d\n" % (tuple(t) + (7, 896)[len(t) - 4:]) for t in triples)
+        inp = "".join("%d %d %d %d %d %d %d %d\n" % (tuple(t) + (7, 896, 896, 9)[len(t) - 4:])
+                      for t in triples)
         out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
         return [tuple(int(v) for v in line.split()) for line in out.splitlines()]
     return run
 
 
-@pytest.mark.parametrize("C", CHUNKS)
+@pytest.mark.parametrize("C,LR,lt", KERNELS)
 @pytest.mark.parametrize("team_max", [1, 3, 26, 128])
 @pytest.mark.parametrize("K", [8, 64, 72, 136, 1032, 2056, 4104, 8192])
-def test_bound_covers_the_worst_split(bound_tool, K, team_max, C):
+def test_bound_covers_the_worst_split(bound_tool, K, team_max, C, LR, lt):
     Mmax, Gmax = 17000, 64
-    lt = WIDEST[C]
-    best = worst_splits(Mmax, K, Gmax, team_max, lt, C)
+    best = worst_splits(Mmax, K, Gmax, team_max, lt, C, LR)
     Ms = [0, 1, 20, 21, 28, 29, 40, 41, 56, 57, 80, 81, 113, 400, 449, 640, 641, 896, 897, 1280, 1281,
           1793, 1921, 5120, 5121, 6000, 10242, 12000, 16640, 17000]
     Gs = [1, 2, 3, 7, 16, 64]
-    triples = [(M, K, G, team_max, lt, C) for M in Ms for G in Gs]
+    triples = [(M, K, G, team_max, lt, C, LR) for M in Ms for G in Gs]
     got = bound_tool(triples)
-    for (M, _, G, _, _, _), (b, _, one) in zip(triples, got):
+    for (M, _, G, _, _, _, _), (b, _, one) in zip(triples, got):
         exact = int(best[G][M])
-        assert b >= exact, (M, K, G, team_max, C, b, exact)
+        assert b >= exact, (M, K, G, team_max, C, LR, b, exact)
         # and it is no wild over-estimate (the grid's extra workgroups exit at once)
-        assert b <= 2 * exact + 16, (M, K, G, team_max, C, b, exact)
-        assert one == tiles(M, K, team_max, lt, C)
+        assert 2 * b <= 3 * exact + 32, (M, K, G, team_max, C, LR, b, exact)
+        assert one == tiles(M, K, team_max, lt, C, LR)
 
 
-@pytest.mark.parametrize("C", CHUNKS)
+@pytest.mark.parametrize("LR", [896, 640])
 @pytest.mark.parametrize("max_lt", [3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("K", [64, 1032, 4096, 8200])
-def test_bound_with_narrowed_strips(bound_tool, K, max_lt, C):
+def test_bound_with_narrowed_strips(bound_tool, K, max_lt, LR):
+    C = C896
     team_max = 128
     Mmax, Gmax = 17000, 64
-    best = worst_splits(Mmax, K, Gmax, team_max, max_lt, C)
+    best = worst_splits(Mmax, K, Gmax, team_max, max_lt, C, LR)
     Ms = [0, 1, 20, 21, 29, 41, 57, 80, 81, 113, 161, 225, 321, 449, 640, 641, 897, 1281, 4096, 6000,
           16640, 17000]
     Gs = [1, 2, 4, 16, 64]
-    triples = [(M, K, G, team_max, max_lt, C) for M in Ms for G in Gs]
+    triples = [(M, K, G, team_max, max_lt, C, LR) for M in Ms for G in Gs]
     got = bound_tool(triples)
-    for (M, _, G, _, _, _), (b, _, one) in zip(triples, got):
+    for (M, _, G, _, _, _, _), (b, _, one) in zip(triples, got):
         exact = int(best[G][M])
-        assert exact <= b <= 2 * exact + 16, (M, K, G, max_lt, C, b, exact)
-        assert one == tiles(M, K, team_max, max_lt, C)
+        assert exact <= b and 2 * b <= 3 * exact + 32, (M, K, G, max_lt, C, LR, b, exact)
+        assert one == tiles(M, K, team_max, max_lt, C, LR)
 
 
 def test_strip_cap_policy(bound_tool):
@@ -145,25 +156,25 @@ def test_strip_cap_policy(bound_tool):
              ((16640, 8192, 64), (9, 7)), ((65536, 4096, 8), (9, 7)), ((16640, 8192, 1), (9, 7)),
              ((81920, 8192, 16), (9, 7)), ((4096, 64, 16), (3, 3)), ((2048, 8192, 64), (9, 7)),
              ((512, 4096, 8), (4, 4)), ((16384, 2048, 512), (8, 7)), ((1024, 1024, 4), (3, 3))]
-    for ci, C in enumerate(CHUNKS):
-        got = bound_tool([(M, K, G, 128, -256, C) for (M, K, G), _ in cases])
+    for ci, (C, LR, widest) in enumerate(KERNELS):
+        got = bound_tool([(M, K, G, 128, -256, C, LR, widest) for (M, K, G), _ in cases])
         for ((M, K, G), want), (lt,) in zip(cases, got):
             assert lt == want[ci], (M, K, G, C, lt, want)
             # what the rule promises: a tile per CU for equal groups, unless the
             # narrowest strips are reached
-            assert lt == 3 or G * tiles(M // G, K, 128, lt, C) >= 256
+            assert lt == 3 or G * tiles(M // G, K, 128, lt, C, LR) >= 256
 
 
-@pytest.mark.parametrize("C", CHUNKS)
-def test_bound_of_the_benchmark_shape(bound_tool, C):
-    (b, chunks, _), = bound_tool([(16640, 8192, 64, 128, WIDEST[C], C)])
-    exact = int(worst_splits(16640, 8192, 64, 128, WIDEST[C], C)[64][16640])
+@pytest.mark.parametrize("C,LR,lt", KERNELS)
+def test_bound_of_the_benchmark_shape(bound_tool, C, LR, lt):
+    (b, chunks, _), = bound_tool([(16640, 8192, 64, 128, lt, C, LR)])
+    exact = int(worst_splits(16640, 8192, 64, 128, lt, C, LR)[64][16640])
     assert exact <= b
     assert chunks == 16640 // C + 16640 // (C + 1)
 
 
-@pytest.mark.parametrize("C", CHUNKS)
-def test_chunk_bound_covers_every_chunked_split(bound_tool, C):
+def test_chunk_bound_covers_every_chunked_split(bound_tool):
+    C = C896
     # the chunked groups of any split have at most dim0_chunk_bound(M, C) chunks
     for M in (C + 1, 2 * C + 1, 2 * C + 2, 3 * C, 3 * C + 1, 4 * C + 2, 8 * C + 1, 16 * C + 2, 16640,
               40000):
@@ -182,14 +193,32 @@ def test_xcd_split_tiles_are_eight_copies(bound_tool, K, max_lt):
     of the tiles of a K / 8-column problem, so 8 x the bound for K / 8 covers
     the launch."""
     assert K % (64 << max_lt) == 0
-    C = 640
+    C, LR = C896, 640
     for team_max in (1, 32):
-        Rs = [0, 1, 16, 80, 81, 161, 321, 640, 641, 1281, 5121, 20481]
-        got = bound_tool([(R, K, 1, team_max, max_lt, C) for R in Rs])
-        part = bound_tool([(R, K // 8, 1, team_max, max_lt, C) for R in Rs])
+        Rs = [0, 1, 16, 80, 81, 161, 321, 640, 641, 896, 897, 1793, 5121, 20481]
+        got = bound_tool([(R, K, 1, team_max, max_lt, C, LR) for R in Rs])
+        part = bound_tool([(R, K // 8, 1, team_max, max_lt, C, LR) for R in Rs])
         for R, (_, _, full), (_, _, eighth) in zip(Rs, got, part):
             assert full == 8 * eighth, (R, K, max_lt, team_max, full, eighth)
         for M, G in ((16640, 64), (3200, 3), (20480, 1)):
-            (b8, _, _), = bound_tool([(M, K // 8, G, team_max, max_lt, C)])
-            exact = int(worst_splits(M, K, G, team_max, max_lt, C)[G][M])
+            (b8, _, _), = bound_tool([(M, K // 8, G, team_max, max_lt, C, LR)])
+            exact = int(worst_splits(M, K, G, team_max, max_lt, C, LR)[G][M])
             assert 8 * b8 >= exact, (M, K, G, team_max, b8, exact)
+
+
+@pytest.mark.parametrize("LR,widest,cases", [(896, 9, "DIM0"), (640, 7, "DIM0_T")])
+def test_lds_row_cases_reach_their_strips(bound_tool, LR, widest, cases):
+    """The GPU tests of rows held in LDS run on the strips they name: the
+    launch's strip cap lets its repeated group keep strips of 8 << lt
+    columns, and that group (and at least one other) lies in the LDS range
+    of those strips."""
+    import lds_row_cases
+    for K, sizes, lt in getattr(lds_row_cases, cases):
+        M, G = sum(sizes), len(sizes)
+        (cap,), = bound_tool([(M, K, G, 128, -256, C896, LR, widest)])
+        assert cap >= lt and min(group_lt(sizes[0], C896, LR), cap) == lt, (K, lt, cap)
+        rps = 512 >> lt
+        in_lds = [R for R in sizes if min(group_lt(R, C896, LR), cap) == lt and 20 * rps < R <= 28 * rps]
+        assert sizes[0] in in_lds and len(set(in_lds)) >= 2, (K, lt, sorted(set(in_lds)))
+        if cases == "DIM0_T":
+            assert all(R % 16 == 0 for R in sizes)

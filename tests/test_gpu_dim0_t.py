@@ -1,7 +1,8 @@
 """GPU parity of the transposed dim0 entry point (mgs_quant_groups_dim0_t):
 q_t (K, M) and scales_t (K, G) against the oracle byte for byte, over every
 strip class (1024- down to 128-column strips, K narrower than a strip,
-ragged last strips), empty groups, chunk teams and column-maximum tiles,
+ragged last strips), tiles with rows held in LDS on every strip width,
+empty groups, chunk teams and column-maximum tiles,
 the path that computes the maxima in the waiting tile itself, pow2 scales,
 the benchmark shape compared whole, and offsets that are not multiples
 of 16 (values unspecified, writes in bounds). Every output carries guard
@@ -15,6 +16,7 @@ import group_scaling_fp8_amd as mgs
 from group_scaling_fp8_amd import workloads as wl
 from gpu_util import Guarded, assert_same_bytes, to_dev
 from oracle_pool import check_dim0_t_whole
+import lds_row_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -49,17 +51,28 @@ def data(seed, M, K):
 
 @pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("K,sizes", [
-    (264, [16, 48, 0, 80, 160, 256, 320, 336, 640]),   # every strip width up to K, ragged K
-    (520, [656, 16, 1296]),                            # two- and three-chunk teams
+    (264, [16, 48, 0, 80, 160, 256, 320, 336, 640, 656, 896]),   # every strip width up to K, ragged K
+    (520, [912, 16, 1808]),                            # two- and three-chunk teams
     (8, [32, 0, 704, 16]),                             # one 8-column strip
     (72, [320, 336, 16]),                              # K narrower than a strip
     (1032, [208, 400, 96]),
-    (2056, [16, 64, 80, 0, 144, 32]),                  # 1024- and 512-column strips
+    (2056, [16, 64, 80, 0, 144, 32, 112, 224, 448]),   # 1024- and 512-column strips
 ])
 def test_dim0_t_classes(K, sizes, pow2):
     off = np.cumsum(sizes).astype(np.int32)
     M = int(off[-1])
     check(data(M + K, M, K), off, "sizes %s K=%d" % (sizes, K), pow2)
+
+
+# Tiles whose rows run past the registers into LDS (cast there, then staged
+# before the register rows), on every strip width of the transposed kernel
+# (tests/lds_row_cases.py, whose strips a CPU test checks).
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("K,sizes", [(K, sizes) for K, sizes, _ in lds_row_cases.DIM0_T])
+def test_dim0_t_rows_held_in_lds(K, sizes, pow2):
+    off = np.cumsum(sizes).astype(np.int32)
+    M = int(off[-1])
+    check(data(M + K, M, K), off, "LDS rows K=%d %s" % (K, sizes[-5:]), pow2)
 
 
 def test_dim0_t_no_rows_writes_scales():

@@ -19,6 +19,7 @@ import oracle
 import group_scaling_fp8_amd as mgs
 from group_scaling_fp8_amd import workloads as wl
 from gpu_util import Guarded, assert_same_bytes, to_dev
+import lds_row_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -67,10 +68,10 @@ TEAM_MAX = [None, 1]      # the library's limit, then every tall group through m
 
 # The first row count of each tiling step has the most tiles per row: 29 rows
 # (2048-column strips), 57 (1024), 113 (512), 225 (256), 449 (128), then
-# 896 * (c - 1) + 1 rows for a group cut into c chunks (897: two); the
-# transposed kernel's steps (81, 161, 321, 641, ...) are covered too. K values
-# leave a ragged last strip, and the launches make at least one tile per CU,
-# so their strips are not narrowed.
+# 896 * (c - 1) + 1 rows for a group cut into c chunks (897: two); 81, 161,
+# 321 and 641 are the first rows held in LDS on 1024- to 128-column strips.
+# K values leave a ragged last strip. Launches with fewer tiles than compute
+# units get narrower strips, which the grid bound covers as well.
 @pytest.mark.parametrize("team_max", TEAM_MAX)
 @pytest.mark.parametrize("size,n,K", [
     (113, 12, 2056), (225, 12, 1032), (449, 8, 520), (897, 6, 264), (1793, 3, 264),
@@ -87,23 +88,15 @@ def test_most_tiles_per_row(size, n, K, team_max):
 
 
 # Tiles whose rows run past the 20 register slabs into the LDS slabs, for
-# every strip width: rows 20 * rps .. 28 * rps - 1 (rps = 1, 2, 4, 8, 16, 32
-# rows per slab), with ragged last slabs, ragged K and empty groups beside
-# them (the widest strips need enough tiles for one per CU).
+# every strip width (tests/lds_row_cases.py, whose strips a CPU test checks),
+# and on one 8-column strip.
 @pytest.mark.parametrize("pow2", [False, True])
-@pytest.mark.parametrize("K,sizes", [
-    (8200, [28] * 90 + [20, 27, 0, 5]),    # 4096-column strips, rps = 1
-    (4104, [56] * 100 + [40, 55, 1]),      # 2048, rps = 2
-    (2056, [81, 100, 0, 112, 7]),          # 1024-column strips, rps = 4
-    (1032, [161, 200, 224, 3]),            # 512, rps = 8
-    (520, [321, 400, 448, 16]),            # 256, rps = 16
-    (264, [641, 700, 896, 5, 0]),          # 128, rps = 32
-    (8, [700, 896, 1]),                    # one 8-column strip
-])
+@pytest.mark.parametrize("K,sizes", [(K, sizes) for K, sizes, _ in lds_row_cases.DIM0] +
+                         [(8, [700, 896, 1])])
 def test_rows_held_in_lds(K, sizes, pow2):
     off = np.cumsum(sizes).astype(np.int32)
     x = data(sum(sizes) + K, int(off[-1]), K)
-    check(x, off, "LDS rows %s" % (sizes,), pow2)
+    check(x, off, "LDS rows K=%d %s" % (K, sizes[-6:]), pow2)
 
 
 def test_group_past_the_team_limit():

@@ -199,7 +199,7 @@ def test_dim1_no_columns_writes_scales(M, pow2):
     (6000, 64, [5120, 880]),                     # chunked, with 64-column rows
     (2600, 264, [1280, 1281, 39]),               # two chunked groups and a short one
     (1300, 264, [576, 577, 147]),                # 128-column strips with a ragged last slab
-    (1300, 264, [640, 641, 19]),                 # either side of dim0_t's chunking threshold
+    (1300, 264, [640, 641, 19]),                 # either side of a 128-column tile's register rows
     (2000, 264, [896, 897, 207]),                # either side of dim0's chunking threshold
 ])
 def test_dim0_edges(M, K, sizes, pow2):

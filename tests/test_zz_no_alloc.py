@@ -67,7 +67,7 @@ def test_noalloc_matches_the_workspace_entry_point(pow2):
 def test_noalloc_refuses_inputs_beyond_its_array():
     L = mgs.lib()
     need = ctypes.c_int64(0)
-    M, K = 200000, 8192
+    M, K = 300000, 8192
     assert L.mgs_dim0_workspace_bytes(M, K, ctypes.byref(need)) == mgs.MGS_OK
     assert need.value > mgs._lib.MGS_NOALLOC_SCRATCH_BYTES
     A = 1 << 20     # never dereferenced: the size check comes first
