@@ -194,6 +194,22 @@ __device__ __forceinline__ void write_lanes16(int& v, const int32_t* __restrict_
     write_lane<L + 15>(v, e[15]);
 }
 
+// The lane number, computed where it is used: the compiler cannot hoist it,
+// so addresses derived from it do not stay live (and spill) across the
+// whole kernel.
+__device__ __forceinline__ int lane_here() {
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    return lane;
+}
+
+// threadIdx.x through an opaque copy, for the same reason.
+__device__ __forceinline__ int tid_here() {
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    return tid;
+}
+
 // Lane i's raw group end for group base + i: off[base + i] (or the equal
 // group's end), M past the last group. kScalar: the offsets come in through
 // scalar loads, 16 at a time, and are written into lanes with v_writelane.
@@ -204,7 +220,9 @@ __device__ __forceinline__ void write_lanes16(int& v, const int32_t* __restrict_
 template <bool kScalar>
 __device__ __forceinline__ int group_end_raw(const int32_t* __restrict__ off, int base, int G, int M,
                                              int uniform_rows) {
-    const int lane = threadIdx.x & (kWave - 1);
+    // (the lane through lane_here: computed here, not hoisted out of the
+    // tile loop and kept, or spilled, through the whole kernel)
+    const int lane = lane_here();
     if (uniform_rows >= 0) {
         const int g = base + lane;
         return g < G ? (g + 1) * uniform_rows : M;
@@ -232,6 +250,7 @@ __device__ __forceinline__ int group_end_raw(const int32_t* __restrict__ off, in
 
 // Fills t from lane src's group, tile `local` inside that group. src is
 // wave-uniform, so the fields land in scalar registers.
+template <int kRows, bool kScalar>
 __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chunk_incl, int src,
                                           int g, int local, int maxima, int row_align) {
     const int ns = __builtin_amdgcn_readlane(gi.ns, src);
@@ -262,10 +281,23 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
     const int rem = local - quo * den;
     t.strip = team ? quo : rem;
     t.c = team ? rem : quo;
-    // chunk rows, rounded up to row_align (a power of two; at most 640 still)
-    const int cs = ((R + nc - 1) / nc + row_align - 1) & -row_align;
-    t.r0 = min(start + t.c * cs, t.g1);
-    t.r1 = min(start + (t.c + 1) * cs, t.g1);
+    // Chunk rows: R / nc rounded up to row_align (a power of two), or in the
+    // transposed kernel to kLine = 128 rows, a q_t line. kRows is a multiple
+    // of either, so cs <= kRows, and (nc - 1) * cs < R since R > (nc - 1) *
+    // kRows: the last chunk is never empty. The transposed kernel also puts
+    // the boundaries on multiples of 128 rows of x when the last chunk still
+    // fits (chunk 0 then starts short), so that chunk tiles share no q_t line.
+    constexpr int kLine = kScalar ? 1 : 128;
+    static_assert(kRows % 128 == 0, "chunk rounding");
+    const int align = kLine > row_align ? kLine : row_align;
+    const int cs = ((R + nc - 1) / nc + align - 1) & -align;
+    int s0 = start;
+    if (kLine > 1) {
+        const int lead = start & (kLine - 1);
+        if (R + lead - (nc - 1) * cs <= kRows) s0 = start - lead;
+    }
+    t.r0 = t.c == 0 ? start : min(s0 + t.c * cs, t.g1);
+    t.r1 = t.c == nc - 1 ? t.g1 : min(s0 + (t.c + 1) * cs, t.g1);
     t.cbase = __builtin_amdgcn_readlane(chunk_incl, src) - __builtin_amdgcn_readlane(gi.chunks, src);
 }
 
@@ -298,7 +330,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
             const int src = __ffsll((unsigned long long)hx) - 1;
             const int local = target - (__builtin_amdgcn_readlane(incl_x, src) -
                                         __builtin_amdgcn_readlane(gi.cnt_x, src));
-            take_tile(t, gi, incl_ch, src, base + src, local, 1, row_align);
+            take_tile<kRows, kScalar>(t, gi, incl_ch, src, base + src, local, 1, row_align);
             return t;
         }
         if (t.g < 0) {
@@ -307,7 +339,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
                 const int src = __ffsll((unsigned long long)hm) - 1;
                 const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
                                             __builtin_amdgcn_readlane(gi.cnt_m, src));
-                take_tile(t, gi, incl_ch, src, base + src, local, 0, row_align);
+                take_tile<kRows, kScalar>(t, gi, incl_ch, src, base + src, local, 0, row_align);
             }
         }
         if (t.g >= 0 && !maybe_c) return t;
@@ -335,7 +367,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
             const int src = __ffsll((unsigned long long)hm) - 1;
             const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
                                         __builtin_amdgcn_readlane(gi.cnt_m, src));
-            take_tile(t, gi, incl_ch, src, base + src, local, 0, row_align);
+            take_tile<kRows, kScalar>(t, gi, incl_ch, src, base + src, local, 0, row_align);
             return t;
         }
         carry_end = __builtin_amdgcn_readlane(end, kWave - 1);
@@ -437,8 +469,8 @@ __device__ Tile find_tile_wide(const int32_t* __restrict__ off, int G, int M, in
         if (h && t.g < 0) {
             const int src = __ffsll((unsigned long long)h) - 1;
             const int local = tgt - (__builtin_amdgcn_readlane(incl, src) - __builtin_amdgcn_readlane(cnt, src));
-            take_tile(t, gi[p], base_ch + incl_ch[p], src, b0 + p * kWave + src, local, maxima ? 1 : 0,
-                      row_align);
+            take_tile<kRows, kScalar>(t, gi[p], base_ch + incl_ch[p], src, b0 + p * kWave + src, local,
+                                      maxima ? 1 : 0, row_align);
         }
     }
     if (t.g >= 0 && lane == 0) {
@@ -466,22 +498,6 @@ __device__ Tile find_tile_wide(const int32_t* __restrict__ off, int G, int M, in
         r.cbase = __builtin_amdgcn_readfirstlane(d[11]);
     }
     return r;
-}
-
-// The lane number, computed where it is used: the compiler cannot hoist it,
-// so addresses derived from it do not stay live (and spill) across the
-// whole kernel.
-__device__ __forceinline__ int lane_here() {
-    int lane;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-    return lane;
-}
-
-// threadIdx.x through an opaque copy, for the same reason.
-__device__ __forceinline__ int tid_here() {
-    int tid;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
-    return tid;
 }
 
 __device__ __forceinline__ void max4(uint4& m, const uint4& t) {
@@ -518,6 +534,21 @@ __device__ __forceinline__ uint4 block_column_amax(uint4 m, int tpr, uint4* red)
     uint4 a = make_uint4(0u, 0u, 0u, 0u);
     for (int p = 0; p < parts; ++p) max4(a, red[p * tpr + tx]);
     return a;
+}
+
+// Whether ok holds in every thread of the workgroup: a ballot per wave, one
+// LDS word per wave, one barrier. (HIP's __syncthreads_and reduces over the
+// flat thread id, which keeps the y and z thread ids in registers through
+// the whole kernel.) Called at most once per tile item: vote is written again
+// only in a later item, after the item's closing barrier.
+__device__ __forceinline__ bool block_all(bool ok, int* vote) {
+    const unsigned long long bad = __ballot(!ok);
+    if (lane_here() == 0) vote[threadIdx.x / kWave] = bad == 0ull;
+    __syncthreads();
+    int all = 1;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) all &= vote[w];
+    return all != 0;
 }
 
 struct TileGeom {
@@ -579,6 +610,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // lane i of a wave writes 16 bytes at the wave's LDS base + 16 i), so thread
 // t owns ext[e * kThreads + t]. Lanes whose row or columns do not exist load
 // nothing, and ext_slab masks them.
+// In the quad layout tile rows are whole quads (the transposed kernel's rows
+// and row starts are multiples of 16), so a quad's first row decides for all
+// four of its vectors.
+template <bool kQuad>
+__device__ __forceinline__ int ext_check_row(int e, int rps, int ty) {
+    return slab_row<kQuad>(reg_slabs<kQuad>() + (kQuad ? e & ~3 : e), rps, ty);
+}
+
 template <bool kQuad>
 __device__ __forceinline__ void load_tile_ext(const uint16_t* __restrict__ x, int64_t K, int r0,
                                               int nrows, const TileGeom& q, uint4* ext) {
@@ -587,7 +626,7 @@ __device__ __forceinline__ void load_tile_ext(const uint16_t* __restrict__ x, in
     const uint16_t* p = x + (int64_t)(r0 + slab_row<kQuad>(kSlabs, q.rps, q.ty)) * K + q.col;
 #pragma unroll
     for (int e = 0; e < kLdsSlabs; ++e) {
-        const int r = slab_row<kQuad>(kSlabs + e, q.rps, q.ty);
+        const int r = ext_check_row<kQuad>(e, q.rps, q.ty);
         if (r < nrows && q.col_ok)
             __builtin_amdgcn_global_load_lds(p, (lds_void*)(ext + e * kThreads + wave * kWave), 16, 0,
                                              kLoadNontemporal);
@@ -598,7 +637,7 @@ __device__ __forceinline__ void load_tile_ext(const uint16_t* __restrict__ x, in
 
 template <bool kQuad>
 __device__ __forceinline__ uint4 ext_slab(const uint4* ext, int e, int nrows, const TileGeom& q) {
-    if (slab_row<kQuad>(reg_slabs<kQuad>() + e, q.rps, q.ty) < nrows && q.col_ok)
+    if (ext_check_row<kQuad>(e, q.rps, q.ty) < nrows && q.col_ok)
         return ext[e * kThreads + threadIdx.x];
     return make_uint4(0u, 0u, 0u, 0u);
 }
@@ -749,7 +788,7 @@ __device__ __forceinline__ void dim0_body(
         int pow2, uint8_t* __restrict__ q, float* __restrict__ scales, int n_tiles, int team_max,
         int lt_cap, int maybe_c, uint32_t* __restrict__ ws_ctr, uint64_t* __restrict__ ws_max,
         long long spin_ticks, int uniform_rows, int xcd_split, uint4* red, uint32_t* stage, uint4* ext,
-        int* search) {
+        int* search, int* vote) {
     constexpr int kRowAlign = kT ? 16 : 1;
     constexpr int kRows = rows_w128<kT>();
     constexpr int kLtRows = kT ? kDim0LtRowsT : kDim0LtRows;
@@ -793,7 +832,7 @@ __device__ __forceinline__ void dim0_body(
             // by tiles earlier in the grid; wait for them before the tile's own
             // loads, so that no tile data sits in registers meanwhile
             const bool ok = gather_maxima(ws_max, t, K, geo, spin_ticks, m);
-            if (!__syncthreads_and(ok)) {
+            if (!block_all(ok, vote)) {
                 m = make_uint4(0u, 0u, 0u, 0u);
                 stream_amax(x, K, t.g0, t.g1 - t.g0, geo, m);
             }
@@ -841,7 +880,7 @@ __device__ __forceinline__ void dim0_body(
             // a complete gather has read this tile's own words back, so they
             // are stored before the tile counts as done
             const bool ok = gather_maxima(ws_max, t, K, geo, spin_ticks, m);
-            if (!__syncthreads_and(ok)) {
+            if (!block_all(ok, vote)) {
                 // the team's maxima did not come in time: the column amax of
                 // the whole group from x
                 m = make_uint4(0u, 0u, 0u, 0u);
@@ -1018,8 +1057,9 @@ __global__ __launch_bounds__(kThreads, 4) void dim0_kernel(
     __shared__ uint4 red[kThreads];
     __shared__ uint4 ext[kLdsSlabs * kThreads];     // 64 KiB: the tile's rows past the registers
     __shared__ int search[kSearchWords];
+    __shared__ int vote[kWaves];
     dim0_body<false>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
-                     ws_max, spin_ticks, uniform_rows, xcd_split, red, nullptr, ext, search);
+                     ws_max, spin_ticks, uniform_rows, xcd_split, red, nullptr, ext, search, vote);
 }
 
 // The same per-group scaling with transposed outputs: qT (K, M), scalesT (K, G).
@@ -1031,9 +1071,10 @@ __global__ __launch_bounds__(kThreads, 4) void dim0t_kernel(
     __shared__ uint4 red[kThreads];
     __shared__ uint4 ext[kLdsSlabs * kThreads];     // 64 KiB: rows past the registers, then the stage
     __shared__ int search[kSearchWords];
+    __shared__ int vote[kWaves];
     dim0_body<true>(x, M, K, off, G, pow2, q, scales, n_tiles, team_max, lt_cap, maybe_c, ws_ctr,
                     ws_max, spin_ticks, uniform_rows, xcd_split, red, reinterpret_cast<uint32_t*>(ext),
-                    ext, search);
+                    ext, search, vote);
 }
 
 // Zero fill of n 16-byte words (a fresh workspace; no memset node, so the

@@ -222,3 +222,51 @@ def test_lds_row_cases_reach_their_strips(bound_tool, LR, widest, cases):
         assert sizes[0] in in_lds and len(set(in_lds)) >= 2, (K, lt, sorted(set(in_lds)))
         if cases == "DIM0_T":
             assert all(R % 16 == 0 for R in sizes)
+
+
+def chunk_rows(start, R, C, row_align, line):
+    """The chunks [r0, r1) of a group of R > C rows starting at row start, as
+    the kernels' tile search cuts them: nc = ceil(R / C) chunks of R / nc rows
+    rounded up to max(row_align, line); with line > 1 (the transposed kernel,
+    128) the boundaries move down to multiples of line when the last chunk
+    still fits."""
+    nc = -(-R // C)
+    align = max(line, row_align)
+    cs = -(-(-(-R // nc)) // align) * align
+    s0 = start
+    if line > 1:
+        lead = start % line
+        if R + lead - (nc - 1) * cs <= C:
+            s0 = start - lead
+    g1 = start + R
+    out = []
+    for c in range(nc):
+        r0 = start if c == 0 else min(s0 + c * cs, g1)
+        r1 = g1 if c == nc - 1 else min(s0 + (c + 1) * cs, g1)
+        out.append((r0, r1))
+    return out
+
+
+@pytest.mark.parametrize("line,row_align", [(1, 1), (128, 16)])
+def test_chunks_cover_the_group(line, row_align):
+    """Chunks partition the group's rows, none is empty or holds more than a
+    tile's C = 896 rows; with 128-row lines every inner boundary of a group
+    whose start is on the 16-row grid lies on a multiple of 128 whenever
+    that keeps the last chunk within C rows, and always on one for groups
+    starting on a line."""
+    C = 896
+    rng = np.random.default_rng(5)
+    Rs = list(range(C + 1, 4 * C + 200, 7)) + [16640, 16640 - 16, 120000, 2080, 8320]
+    for R in Rs:
+        R = R // row_align * row_align
+        if R <= C:
+            continue
+        for start in [0, 16, 112, 128, 4096 + 48] + [int(v) * row_align for v in rng.integers(0, 1000, 4)]:
+            ch = chunk_rows(start, R, C, row_align, line)
+            assert ch[0][0] == start and ch[-1][1] == start + R
+            for (a, b), (c2, _) in zip(ch, ch[1:]):
+                assert b == c2
+            assert all(0 < b - a <= C for a, b in ch), (start, R, ch)
+            assert all(a % row_align == 0 for a, _ in ch)
+            if line > 1 and start % line == 0:
+                assert all(a % line == 0 for a, _ in ch), (start, R, ch)
