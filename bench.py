@@ -41,11 +41,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """Source text without // comments, trailing blanks and blank lines, so
+    that comment edits leave the hash alone (the sources use no string
+    literal that holds //)."""
+    out = []
+    for line in text.splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out) + "\n"
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources' code, comments left out."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "group_scaling_fp8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "group_scaling_fp8_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -37,8 +37,10 @@
 //     otherwise have fewer tiles than CUs (lt_cap, from dim0_lt_cap): rows of
 //     128 bytes stream far worse than rows of 256.
 //   * class T, R > C rows and at most team_max chunks: the group is cut
-//     into c = ceil(R / C) chunks on 128-column strips, and the c tiles of
-//     a strip are consecutive in the grid (a team). Each loads its chunk,
+//     into c = ceil(R / C) chunks of about R / c rows (in the transposed
+//     kernel rounded to 128 rows, with boundaries on 128-row lines of x where
+//     the last chunk allows) on 128-column strips, and the c tiles of a strip
+//     are consecutive in the grid (a team). Each loads its chunk,
 //     writes the chunk's column maxima to a workspace, waits for the maxima
 //     of the other chunks of its strip, and casts its chunk from registers.
 //     team_max is at most the CU count: with two resident workgroups per CU

@@ -279,3 +279,14 @@ def test_product_path_never_imports_the_oracle():
             else:
                 continue
             assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), (name, mods)
+
+
+def test_counter_provenance_hash_ignores_comments():
+    """bench.py reports counter traffic only while the kernel sources' code
+    hash matches the one the counters were taken on: comment and blank-line
+    edits keep the hash, code edits change it."""
+    import bench
+    code = "int f(int a) {  // one\n    return a + 1;\n}\n"
+    assert bench._code_only(code) == bench._code_only("// header\n\n" + code.replace("// one", "// two"))
+    assert bench._code_only(code) != bench._code_only(code.replace("a + 1", "a + 2"))
+    assert len(bench.kernel_source_hash()) == 16
