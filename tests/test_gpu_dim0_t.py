@@ -75,6 +75,37 @@ def test_dim0_t_rows_held_in_lds(K, sizes, pow2):
     check(data(M + K, M, K), off, "LDS rows K=%d %s" % (K, sizes[-5:]), pow2)
 
 
+# Tall groups whose chunk boundaries move onto 128-row lines (the last chunk
+# still fits a tile) or stay at multiples of the chunk size from the group
+# start (it would not), for group starts off the 128-row grid; as teams and,
+# with a team limit of 1, as column-maximum tiles.
+@pytest.mark.parametrize("team_max", [None, 1])
+@pytest.mark.parametrize("sizes", [
+    [16, 1808, 16],          # three chunks on lines: 624, 640, 544 rows
+    [80, 4000, 48],          # five chunks on lines, the first 816 rows
+    [16, 1792, 16],          # two full chunks from an unaligned start
+    [48, 2688, 16],          # three full chunks from an unaligned start
+    [128, 1008, 16],         # an aligned start: 512 + 496
+])
+def test_dim0_t_chunk_boundaries(sizes, team_max):
+    off = np.cumsum(sizes).astype(np.int32)
+    M, K = int(off[-1]), 264
+    x = data(M + len(sizes), M, K)
+    if team_max is None:
+        check(x, off, "chunks %s" % (sizes,))
+        return
+    gq, gs = Guarded((K, M), torch.uint8), Guarded((K, len(off)), torch.float32)
+    mgs.api._test_quant_dim0(to_dev(x), to_dev(off), gq.view, gs.view, transposed=True,
+                             spin_ticks=mgs.api.TEST_DEFAULT_SPIN, team_max=team_max,
+                             workspace=mgs.dim0_workspace(M, K))
+    torch.cuda.synchronize()
+    gq.check()
+    gs.check()
+    rq, rs = oracle.quant_groups_dim0_t(x, off)
+    assert_same_bytes(gs.numpy(), rs, "chunks %s team_max=1 scales_t" % (sizes,))
+    assert_same_bytes(gq.numpy(), rq, "chunks %s team_max=1 q_t" % (sizes,))
+
+
 def test_dim0_t_no_rows_writes_scales():
     x = np.zeros((0, 64), np.uint16)
     off = np.zeros(3, np.int32)
