@@ -252,7 +252,7 @@ __device__ __forceinline__ int group_end_raw(const int32_t* __restrict__ off, in
 
 // Fills t from lane src's group, tile `local` inside that group. src is
 // wave-uniform, so the fields land in scalar registers.
-template <int kRows, bool kScalar>
+template <int kRows, int kLine>
 __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chunk_incl, int src,
                                           int g, int local, int maxima, int row_align) {
     const int ns = __builtin_amdgcn_readlane(gi.ns, src);
@@ -283,14 +283,14 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
     const int rem = local - quo * den;
     t.strip = team ? quo : rem;
     t.c = team ? rem : quo;
-    // Chunk rows: R / nc rounded up to row_align (a power of two), or in the
-    // transposed kernel to kLine = 128 rows, a q_t line. kRows is a multiple
-    // of either, so cs <= kRows, and (nc - 1) * cs < R since R > (nc - 1) *
-    // kRows: the last chunk is never empty. The transposed kernel also puts
-    // the boundaries on multiples of 128 rows of x when the last chunk still
-    // fits (chunk 0 then starts short), so that chunk tiles share no q_t line.
-    constexpr int kLine = kScalar ? 1 : 128;
-    static_assert(kRows % 128 == 0, "chunk rounding");
+    // Chunk rows: R / nc rounded up to row_align and kLine (powers of two;
+    // kLine = 128 rows, a q_t line, in the transposed kernel, else 1). kRows
+    // is a multiple of both, so cs <= kRows, and (nc - 1) * cs < R since
+    // R > (nc - 1) * kRows: the last chunk is never empty. With kLine > 1 the
+    // boundaries also move onto multiples of kLine rows of x when the last
+    // chunk still fits (chunk 0 then starts short), so that chunk tiles share
+    // no q_t line.
+    static_assert(kRows % kLine == 0 && (kLine & (kLine - 1)) == 0, "chunk rounding");
     const int align = kLine > row_align ? kLine : row_align;
     const int cs = ((R + nc - 1) / nc + align - 1) & -align;
     int s0 = start;
@@ -307,7 +307,7 @@ __device__ __forceinline__ void take_tile(Tile& t, const GroupInfo& gi, int chun
 // by every wave of the workgroup; all lanes return the same tile.
 // Group ends come from off (uniform_rows < 0), or are (g + 1) * uniform_rows
 // (equal groups, e.g. the experts of a 3D weight, with no offsets array).
-template <int kRows, int kLtRows, bool kScalar>
+template <int kRows, int kLtRows, bool kScalar, int kLine>
 __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
                           int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -332,7 +332,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
             const int src = __ffsll((unsigned long long)hx) - 1;
             const int local = target - (__builtin_amdgcn_readlane(incl_x, src) -
                                         __builtin_amdgcn_readlane(gi.cnt_x, src));
-            take_tile<kRows, kScalar>(t, gi, incl_ch, src, base + src, local, 1, row_align);
+            take_tile<kRows, kLine>(t, gi, incl_ch, src, base + src, local, 1, row_align);
             return t;
         }
         if (t.g < 0) {
@@ -341,7 +341,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
                 const int src = __ffsll((unsigned long long)hm) - 1;
                 const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
                                             __builtin_amdgcn_readlane(gi.cnt_m, src));
-                take_tile<kRows, kScalar>(t, gi, incl_ch, src, base + src, local, 0, row_align);
+                take_tile<kRows, kLine>(t, gi, incl_ch, src, base + src, local, 0, row_align);
             }
         }
         if (t.g >= 0 && !maybe_c) return t;
@@ -369,7 +369,7 @@ __device__ Tile find_tile(const int32_t* __restrict__ off, int G, int M, int K, 
             const int src = __ffsll((unsigned long long)hm) - 1;
             const int local = target - (__builtin_amdgcn_readlane(incl_m, src) -
                                         __builtin_amdgcn_readlane(gi.cnt_m, src));
-            take_tile<kRows, kScalar>(t, gi, incl_ch, src, base + src, local, 0, row_align);
+            take_tile<kRows, kLine>(t, gi, incl_ch, src, base + src, local, 0, row_align);
             return t;
         }
         carry_end = __builtin_amdgcn_readlane(end, kWave - 1);
@@ -394,7 +394,7 @@ constexpr int kSearchWords = kSearchTile + 12;
 // tile and chunk totals through LDS (three barriers); the wave that holds
 // the target publishes its tile. Same order, same tiles as find_tile; run by
 // every wave, and every lane returns the same tile.
-template <int kRows, int kLtRows, bool kScalar>
+template <int kRows, int kLtRows, bool kScalar, int kLine>
 __device__ Tile find_tile_wide(const int32_t* __restrict__ off, int G, int M, int K, int team_max,
                                int lt_cap, bool maybe_c, int row_align, int uniform_rows, int target,
                                int* sx) {
@@ -471,7 +471,7 @@ __device__ Tile find_tile_wide(const int32_t* __restrict__ off, int G, int M, in
         if (h && t.g < 0) {
             const int src = __ffsll((unsigned long long)h) - 1;
             const int local = tgt - (__builtin_amdgcn_readlane(incl, src) - __builtin_amdgcn_readlane(cnt, src));
-            take_tile<kRows, kScalar>(t, gi[p], base_ch + incl_ch[p], src, b0 + p * kWave + src, local,
+            take_tile<kRows, kLine>(t, gi[p], base_ch + incl_ch[p], src, b0 + p * kWave + src, local,
                                       maxima ? 1 : 0, row_align);
         }
     }
@@ -794,6 +794,7 @@ __device__ __forceinline__ void dim0_body(
     constexpr int kRowAlign = kT ? 16 : 1;
     constexpr int kRows = rows_w128<kT>();
     constexpr int kLtRows = kT ? kDim0LtRowsT : kDim0LtRows;
+    constexpr int kLine = kT ? 128 : 1;      // chunk boundaries on q_t lines (transposed output)
     constexpr int kSlabs = reg_slabs<kT>();
     const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x) < kWave;
 
@@ -810,10 +811,10 @@ __device__ __forceinline__ void dim0_body(
     for (unsigned item = first; item < (unsigned)n_tiles; item += stride) {
         MGS_TRACE_STAMP(tr0);
         Tile t = G > kWave
-                     ? find_tile_wide<kRows, kLtRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
-                                                  uniform_rows, (int)item, search)
-                     : find_tile<kRows, kLtRows, !kT>(off, G, M, Ks, team_max, lt_cap, maybe_c, kRowAlign,
-                                             uniform_rows, (int)item);
+                     ? find_tile_wide<kRows, kLtRows, !kT, kLine>(off, G, M, Ks, team_max, lt_cap, maybe_c,
+                                                                 kRowAlign, uniform_rows, (int)item, search)
+                     : find_tile<kRows, kLtRows, !kT, kLine>(off, G, M, Ks, team_max, lt_cap, maybe_c,
+                                                            kRowAlign, uniform_rows, (int)item);
         if (t.g < 0) break;      // later items of this workgroup lie past the last tile too
         t.strip += xcol * (Ks >> (t.lt + 3));
         const TileGeom geo = tile_geom(t, K);
