@@ -290,3 +290,16 @@ def test_counter_provenance_hash_ignores_comments():
     assert bench._code_only(code) == bench._code_only("// header\n\n" + code.replace("// one", "// two"))
     assert bench._code_only(code) != bench._code_only(code.replace("a + 1", "a + 2"))
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says
+    why, before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
