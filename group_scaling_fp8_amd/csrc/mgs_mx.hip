@@ -27,7 +27,7 @@ namespace mgs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMxVecs = 4;   // 16-byte vectors per lane per workgroup
+constexpr int kMxVecs = 2;   // 16-byte vectors per lane per workgroup (2: 314 us at (131072, 5120), 4: 324, 1: 341, 8: 325)
 
 __global__ __launch_bounds__(kThreads) void mx_kernel(const uint16_t* __restrict__ x, int64_t n_vec,
                                                       int rceil, uint8_t* __restrict__ q,
@@ -219,17 +219,21 @@ __device__ __forceinline__ uint32_t dequant2(uint32_t w, float s) {
     return bf16_rne(f.x * s) | (bf16_rne(f.y * s) << 16);
 }
 
+constexpr int kDqUnits = 2;   // units of 8 codes per lane (at (131072, 5120): 2: 318 us, 1: 332, 4: 329, 8: 339)
+
 __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint2* __restrict__ q,
                                                               const uint8_t* __restrict__ scales,
                                                               int64_t n8, uint4* __restrict__ y) {
-    // units of 8 codes: this wave's 128 units start at wave_base
-    const int64_t wave_base = ((int64_t)blockIdx.x * kThreads + (threadIdx.x & ~(kWave - 1))) * 2;
+    // units of 8 codes: this wave's kDqUnits * 64 units start at wave_base
+    const int64_t wave_base = ((int64_t)blockIdx.x * kThreads + (threadIdx.x & ~(kWave - 1))) * kDqUnits;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t u[2] = {wave_base + lane, wave_base + kWave + lane};
-    uint2 c[2];
-    uint32_t sb[2];
+    int64_t u[kDqUnits];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kDqUnits; ++h) u[h] = wave_base + h * kWave + lane;
+    uint2 c[kDqUnits];
+    uint32_t sb[kDqUnits];
+#pragma unroll
+    for (int h = 0; h < kDqUnits; ++h) {
         c[h] = make_uint2(0u, 0u);
         sb[h] = 0u;
         if (u[h] < n8) {
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint2* __res
         }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kDqUnits; ++h) {
         if (u[h] < n8) {
             const float s = e8m0_value(sb[h]);
             store_stream16(y + u[h], make_uint4(dequant2<false>(c[h].x, s), dequant2<true>(c[h].x, s),
@@ -300,7 +304,7 @@ hipError_t launch_mx_dim1(const uint16_t* x, int64_t M, int64_t K, bool rceil, u
 hipError_t launch_mx_dequant(const uint8_t* q, const uint8_t* scales, int64_t n_elems, uint16_t* y,
                              hipStream_t stream) {
     const int64_t n8 = n_elems / 8;
-    const int64_t per_block = (int64_t)kThreads * 2;
+    const int64_t per_block = (int64_t)kThreads * kDqUnits;
     const int64_t blocks = (n8 + per_block - 1) / per_block;
     hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint2*>(q), scales, n8, reinterpret_cast<uint4*>(y));
